@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Benchmark: ring all-reduce-mean + SGD on one MI355X, N logical ranks in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--algo fused]
+                    [--no-rows] [--no-cpu-baseline] [--profile-mode]
+
+One step = one rar_allreduce_sgd call over the whole workload: every rank's
+gradient is averaged in ring order, the mean is written to every rank, and
+the binary32 weights take one SGD step.  Inputs are seeded synthetic vectors
+already resident in HBM when the timed region starts.
+
+Prints ONE JSON line.  `value` is GB/s of algorithmic bytes (each rank buffer
+read once and written once, w read once and written once: 2*N*P*s + 8*P) per
+second of the timed region.  `roofline` gives the dominant kernel's achieved
+bandwidth from HIP events recorded on the stream the library launches on, against
+MI355X's 8 TB/s HBM3E peak; `traffic` comes from committed rocprofv3 counter
+runs when they were taken on the current kernel source.  `cpu_baseline` is the
+CPU oracle timed on a bounded sample of the same workload.  `rows` measures
+the other paths (ring steps, bf16, buckets, prior-art reducer, plain copy).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import pathlib
+import re
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = ROOT / "ring_all_reduce_amd" / "csrc" / "rar_kernels.hip"
+PROFILES = ROOT / "profiles"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+
+
+def alg_bytes(N, P, es, sgd):
+    return 2 * N * P * es + (8 * P if sgd else 0)
+
+
+def committed_traffic(workload_name: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    f = PROFILES / f"fused_f32_sgd_{workload_name}_pmc.md"
+    if not f.exists():
+        return None
+    m = re.search(r"```json\s*(\{.*?\})\s*```", f.read_text(), re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel_src_sha256_16") != kernel_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, stream):
+    """Run fn() warmup times, then time `steps` calls: per-call HIP events on
+    `stream` (the library's launch stream) plus one event pair around all."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record(stream)
+    for i in range(steps):
+        evs[i][0].record(stream)
+        fn()
+        evs[i][1].record(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in evs]
+    return a.elapsed_time(b), per, wall
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--algo", default="fused", choices=["fused", "ring"])
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-mode", action="store_true",
+                    help="headline kernel and the copy calibration only (for rocprofv3 counter runs)")
+    ap.add_argument("--grid", type=int, default=0, help="max workgroups per launch (0: library default)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: N logical ranks share one device's HBM; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ring_all_reduce_amd import api, synth
+    api.rar_version()  # fail now if the HIP library is missing
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    wl = synth.WORKLOADS[args.workload]
+    if wl.layers:
+        raise SystemExit("the headline step is a flat workload; bucketed timing is in rows")
+    N, P = wl.N, wl.P
+    es = 4 if wl.dtype == "f32" else 2
+    sgd = wl.lr is not None
+    log(f"workload {wl.name}: N={N} P={P} dtype={wl.dtype} sgd={sgd} algo={args.algo}")
+
+    bufs = synth.rank_gradients(wl, dev)
+    w = synth.weights(wl, dev) if sgd else None
+    plan = api.rar_plan(N, P, api.F32 if es == 4 else api.BF16, api.BALANCED)
+    api.rar_plan_set_algo(plan, api.FUSED if args.algo == "fused" else api.RING)
+    if args.grid:
+        api.rar_plan_set_grid(plan, args.grid)
+    torch.cuda.synchronize()
+
+    def step():
+        if sgd:
+            api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream)
+        else:
+            api.rar_allreduce_mean(plan, bufs, P, stream)
+
+    nbytes = alg_bytes(N, P, es, sgd)
+
+    if args.profile_mode:
+        cal = CopyCalibration(dev)
+        for _ in range(args.warmup + args.steps):
+            step()
+            cal.run_once(stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_mode": True, "workload": wl.name, "launches": args.warmup + args.steps,
+                          "copy_bytes_per_launch": cal.bytes, "kernel_src_sha256_16": kernel_sha()}))
+        return
+
+    total_ms, per_ms, wall = time_launches(step, args.steps, args.warmup, stream)
+    ms_per_step = total_ms / args.steps
+    kern_ms = sum(per_ms) / len(per_ms)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    log(f"headline: {ms_per_step:.4f} ms/step, kernel avg {kern_ms:.4f} ms (min {min(per_ms):.4f}), "
+        f"{achieved:.1f} GB/s = {achieved / PEAK_HBM_GBS:.3f} of peak; wall {wall:.3f} s")
+
+    out = {
+        "metric": "all-reduce-mean GB/s (bytes read+written) & % HBM peak, 10 ranks x 300M fp32",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if es == 4 else "bf16",
+        "data": "synthetic (seeded normal gradients, uniform weights, resident in HBM)",
+        "config": {"workload": wl.name, "ranks": N, "elems_per_rank": P, "op": "mean+sgd" if sgd else "mean",
+                   "lr": wl.lr, "chunking": "balanced", "algo": args.algo,
+                   "algorithmic_bytes_per_step": nbytes},
+        "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "params_per_s": round(P / (ms_per_step * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"rar_fused_{'f32' if es == 4 else 'bf16'}" if args.algo == "fused" else "ring steps",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": committed_traffic(wl.name) if args.algo == "fused" else None,
+            "algorithmic_bytes_per_launch": nbytes,
+            "avg_launch_ms": round(kern_ms, 5),
+        },
+    }
+    del bufs, w
+    torch.cuda.empty_cache()
+
+    if not args.no_rows:
+        out["rows"] = secondary_rows(dev, stream)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, dev)
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Plain copy calibration (known bytes), also the copy-ceiling row
+# ---------------------------------------------------------------------------
+
+class CopyCalibration:
+    """A 1.2 GB device-to-device copy through the library's own dwordx4 copy
+    kernel (bucket pack of one tensor): bytes moved are known exactly."""
+
+    def __init__(self, dev, elems=300_000_000):
+        import torch
+        from ring_all_reduce_amd import api
+        self.src = torch.ones(elems, dtype=torch.float32, device=dev)
+        self.dst = torch.empty_like(self.src)
+        self.b = api.rar_bucket_plan([elems], api.F32, elems * 4)
+        self.bytes = 2 * elems * 4
+
+    def run_once(self, stream):
+        from ring_all_reduce_amd import api
+        api.rar_bucket_pack(self.b, 0, [[self.src]], [self.dst], stream)
+
+
+# ---------------------------------------------------------------------------
+# Other rows
+# ---------------------------------------------------------------------------
+
+def secondary_rows(dev, stream, reps=5):
+    import torch
+    from ring_all_reduce_amd import api, synth
+    rows = []
+
+    def add(name, nbytes, fn, moved=None, extra=None):
+        total, per, _ = time_launches(fn, reps, 2, stream)
+        ms = total / reps
+        r = {"row": name, "ms": round(ms, 4), "alg_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+             "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if moved:
+            r["moved_GBps"] = round(moved / (ms * 1e-3) / 1e9, 1)
+        if extra:
+            r.update(extra)
+        rows.append(r)
+        log(f"row {name}: {r}")
+
+    # plain copy ceiling: torch's copy and the library's own copy kernel
+    cal = CopyCalibration(dev)
+    add("copy_1.2GB_rar_copy_kernel", cal.bytes, lambda: cal.run_once(stream))
+    add("copy_1.2GB_torch_copy_", cal.bytes, lambda: cal.dst.copy_(cal.src))
+    del cal
+    torch.cuda.empty_cache()
+
+    # workloads 2 and 3 (binary32, SGD): fused, ring steps, reduce-scatter + owner SGD
+    # + weight all-gather, and the prior-art single reducer
+    for key in (2, 3):
+        wl = synth.WORKLOADS[key]
+        N, P = wl.N, wl.P
+        bufs = synth.rank_gradients(wl, dev)
+        w = synth.weights(wl, dev)
+        nb = alg_bytes(N, P, 4, True)
+        for algo, an in ((api.FUSED, "fused"), (api.RING, "ring"), (api.NAIVE, "naive_reducer")):
+            plan = api.rar_plan(N, P)
+            api.rar_plan_set_algo(plan, algo)
+            moved = None if algo == api.FUSED else 5 * (N - 1) * P * 4 + 8 * P
+            add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream), moved,
+                {"algo": an})
+        if key == 3:
+            wreps = [w] + [w.clone() for _ in range(N - 1)]
+            plan = api.rar_plan(N, P)
+            moved = 3 * (N - 1) * P * 4 + 8 * P + 2 * (N - 1) * P * 4
+            add(f"{wl.name}_reduce_scatter_sgd_allgather", nb,
+                lambda: api.rar_reduce_scatter_sgd_allgather(plan, bufs, wreps, wl.lr, P, stream), moved,
+                {"algo": "rs_sgd_ag"})
+            del wreps
+        del bufs, w
+        torch.cuda.empty_cache()
+
+    # workload 5: bf16 storage, binary32 accumulation, 40 ranks
+    wl = synth.WORKLOADS[5]
+    N, P = wl.N, wl.P
+    bufs = synth.rank_gradients(wl, dev)
+    w = synth.weights(wl, dev)
+    nb = alg_bytes(N, P, 2, True)
+    for algo, an in ((api.FUSED, "fused"), (api.RING, "ring")):
+        plan = api.rar_plan(N, P, api.BF16)
+        api.rar_plan_set_algo(plan, algo)
+        add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream), None,
+            {"algo": an})
+        del plan
+    del bufs, w
+    torch.cuda.empty_cache()
+
+    # workload 4: Transformer tensor list in 25 MB buckets, 8 ranks
+    wl = synth.WORKLOADS[4]
+    specs, ranks = synth.transformer_rank_tensors(wl, dev)
+    tensors = [ts for (_, ts) in ranks]
+    numels = [s.numel for s in specs]
+    b = api.rar_bucket_plan(numels, api.F32, wl.bucket_bytes)
+    nbk, mx = api.rar_bucket_count(b)
+    bucket_bufs = [torch.empty(mx, dtype=torch.float32, device=dev) for _ in range(wl.N)]
+    total = sum(numels)
+    nb = alg_bytes(wl.N, total, 4, False)
+    add(f"{wl.name}_pack_reduce_unpack", nb,
+        lambda: api.rar_bucket_allreduce_mean(b, tensors, bucket_bufs, api.BALANCED, api.FUSED, stream),
+        3 * nb, {"buckets": nbk})
+    # zero-copy: the tensors are views of one flat arena per rank, in backward
+    # order, so bucket k is a slice of every arena and needs no packing
+    arenas = [flat for (flat, _) in ranks]
+    infos = [api.rar_bucket_info(b, k) for k in range(nbk)]
+    plans = {}
+    for (_, el, _) in infos:
+        if el not in plans:
+            plans[el] = api.rar_plan(wl.N, el)
+
+    def arena_step():
+        for (so, el, _) in infos:
+            api.rar_allreduce_mean(plans[el], [a[so:so + el] for a in arenas], el, stream)
+    add(f"{wl.name}_zero_copy_arena", nb, arena_step, None, {"buckets": nbk})
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, dev, sample_P=60_000_000, min_s=10.0, max_s=30.0):
+    import numpy as np
+    import oracle
+    from ring_all_reduce_amd import synth
+    P = min(sample_P, wl.P)
+    N = wl.N
+    g = [t.cpu().numpy() for t in synth.rank_gradients(wl, dev, P=P)]
+    w = synth.weights(wl, dev, P=P).cpu().numpy()
+    off = oracle.partition(N, P)
+    runs, t_sum = 0, 0.0
+    while t_sum < min_s and runs < 20:
+        t0 = time.perf_counter()
+        oracle.ring_allreduce_f32(g, off, w, wl.lr or 0.0)
+        t_sum += time.perf_counter() - t0
+        runs += 1
+        if t_sum > max_s:
+            break
+    per = t_sum / runs
+    nb = alg_bytes(N, P, 4, wl.lr is not None)
+    return {"value": round(nb / per / 1e9, 3), "unit": "GB/s", "cores": oracle.get_threads(), "kind": "oracle",
+            "sample": f"{N} ranks x {P} fp32 elements (first {P} of the workload's shape, same seeds and "
+                      f"distribution), literal ring with SGD, {runs} runs, {per:.3f} s per run",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * rar.h -- C ABI of librar.so: ring all-reduce-mean and the synchronous SGD
+ * update of data-parallel training, for N logical ranks whose gradient
+ * buffers all sit in the HBM of one MI355X (gfx950).
+ *
+ * Sources (short names):
+ *   [Gibiansky]  "Bringing HPC Techniques to Deep Learning", A. Gibiansky,
+ *                Baidu SVAIL (Korean translation at wonjae.kim).
+ *   [TrainMGPU]  "[AI System] Training With Multiple GPUs".
+ *   [DDPpage]    "[PyTorch] GPU 분산 학습 1 - DP / DDP / FSDP 개념".
+ *
+ * The problem ([Gibiansky] §Scatter-reduce, opening paragraph): N ranks each
+ * hold an array of the same length P; afterwards every rank holds the same
+ * array.  Here that array is the element-wise MEAN of the N inputs, because
+ * data-parallel SGD averages the per-rank gradients and applies the average
+ * to the weights ([Gibiansky] §The communication problem; [TrainMGPU]
+ * §Training Process, steps 2-3; [DDPpage] §DDP: every rank ends with the
+ * identical gradient and updates on its own).
+ *
+ * Numerics contract (binary32):
+ *   - Chunk c of the plan's chunk table is summed in ring order, starting at
+ *     rank c: ((g_c + g_{c+1}) + g_{c+2}) + ... + g_{c+N-1} (ranks mod N).
+ *     That is the order the scatter-reduce of [Gibiansky] §Scatter-reduce
+ *     produces (rank n starts by sending chunk n).
+ *   - mean = S / N, one correctly rounded IEEE division.
+ *   - SGD: w = w - (lr * mean), the product and the difference each rounded
+ *     once (no fused multiply-add).
+ *   - No flush of subnormals; NaN and infinity propagate.
+ *   With these, every algorithm below gives bit-identical results.
+ * bf16: values are widened exactly to binary32, summed and divided as above,
+ * and each bf16 buffer receives the mean rounded to nearest-even; the SGD
+ * update uses the binary32 mean.
+ *
+ * Memory and streams: every device pointer is owned by the caller and must
+ * stay valid until the work enqueued on `stream` (a hipStream_t passed as
+ * void*, NULL = the default stream) has finished.  Calls return after
+ * enqueueing; they never synchronise.  Device pointers must be 16-byte
+ * aligned.  No call allocates device memory except rar_plan_set_algo for a
+ * bf16 ring plan (its binary32 workspace) and rar_bucket_allreduce_mean
+ * (nothing: it takes the caller's bucket buffers).
+ *
+ * Errors: every argument is checked before any device work is enqueued; on
+ * error nothing is enqueued and a negative rar_status is returned.
+ * RAR_EHIP means a HIP call failed; hipGetLastError() has the detail.
+ * Thread safety: a plan is immutable after rar_plan_set_algo; a plan without
+ * a workspace may be used from several host threads and streams at once.  A
+ * bf16 ring plan owns one workspace and must be used by one stream at a time.
+ */
+#ifndef RAR_H
+#define RAR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RAR_MAX_RANKS 64
+
+typedef struct rar_plan_s *rar_plan_t;
+typedef struct rar_buckets_s *rar_buckets_t;
+
+typedef enum { RAR_F32 = 0, RAR_BF16 = 1 } rar_dtype;
+
+/* How P elements are cut into N chunks ([Gibiansky] §Scatter-reduce: the
+ * array is split into N chunks; the page does not say how when N does not
+ * divide P). */
+typedef enum {
+    RAR_CHUNK_BALANCED = 0, /* sizes differ by at most 1, larger chunks first */
+    RAR_CHUNK_CEIL = 1,     /* ceil(P/N) each; the tail takes the rest (may be short or empty) */
+    RAR_CHUNK_ALIGN16 = 2   /* ceil(P/N) rounded up to whole 16-byte groups; tail as CEIL */
+} rar_chunking;
+
+typedef enum {
+    RAR_ALGO_FUSED = 0, /* one pass: reads every rank once, writes every rank once */
+    RAR_ALGO_RING = 1,  /* the 2(N-1) ring steps of [Gibiansky], one kernel per step */
+    RAR_ALGO_NAIVE = 2  /* prior art: rank 0 reduces all and sends back ([Gibiansky]
+                           §The communication problem); its own summation order */
+} rar_algo;
+
+typedef enum {
+    RAR_OK = 0,
+    RAR_EINVAL = -1,    /* bad argument */
+    RAR_EMISMATCH = -2, /* P differs from the plan's P */
+    RAR_EALIGN = -3,    /* a device pointer is not 16-byte aligned */
+    RAR_ENOMEM = -4,    /* host or device allocation failed */
+    RAR_EHIP = -5       /* a HIP runtime call or kernel launch failed */
+} rar_status;
+
+/* ---------------------------------------------------------------------- */
+/* Plans                                                                   */
+/* ---------------------------------------------------------------------- */
+
+/* Create a plan for N ranks (1..RAR_MAX_RANKS) of P >= 0 elements of dtype,
+ * cut into chunks by `chunking` ([Gibiansky] §Scatter-reduce).  Host memory
+ * only; no HIP call.  *out receives the plan (NULL on error).  The algorithm
+ * starts as RAR_ALGO_FUSED. */
+rar_status rar_plan(int N, int64_t P, rar_dtype dtype, rar_chunking chunking, rar_plan_t *out);
+
+/* Free the plan and its workspace (if any).  Waits for the device to finish
+ * work that may use the workspace.  NULL is accepted. */
+rar_status rar_plan_destroy(rar_plan_t plan);
+
+/* Select the algorithm used by rar_allreduce_mean / rar_allreduce_sgd.
+ * For a bf16 plan, RAR_ALGO_RING allocates the binary32 workspace (4*P
+ * bytes, chunk-indexed: it carries the running partial sum of each chunk
+ * between ring steps); RAR_ENOMEM if that fails.  RAR_ALGO_NAIVE is
+ * supported for RAR_F32 only. */
+rar_status rar_plan_set_algo(rar_plan_t plan, rar_algo algo);
+
+/* Kernel launch shape: at most max_blocks workgroups per launch (0 = the
+ * library's choice).  Results do not depend on it. */
+rar_status rar_plan_set_grid(rar_plan_t plan, int max_blocks);
+
+/* Chunk c: element offset and length, and the rank that holds the finished
+ * chunk after scatter-reduce, (c-1) mod N (derived from [Gibiansky]
+ * §Scatter-reduce, and the step-1 table of §Allgather where GPU n starts by
+ * sending chunk n+1).  Any output pointer may be NULL. */
+rar_status rar_plan_chunk(rar_plan_t plan, int c, int64_t *offset, int64_t *length, int *owner_rank);
+
+/* Elements rank `rank` sends and receives in the ring schedule (N-1
+ * scatter-reduce plus N-1 all-gather transfers, [Gibiansky] §Allreduce
+ * communication cost): 2P - |C(rank+1)| - |C(rank+2)| sent and
+ * 2P - |C(rank)| - |C(rank+1)| received, i.e. 2(N-1)P/N when N divides P. */
+rar_status rar_plan_traffic(rar_plan_t plan, int rank, int64_t *sent_elems, int64_t *recv_elems);
+
+/* ---------------------------------------------------------------------- */
+/* All-reduce                                                              */
+/* ---------------------------------------------------------------------- */
+
+/* In place: every bufs[n] (n < N; device, P elements of the plan's dtype)
+ * ends holding the element-wise mean of the N inputs.  bufs is a host
+ * array of N device pointers; it is copied, so it need not outlive the
+ * call.  The N buffers must not overlap.  P must equal the plan's P (it is
+ * passed again as a check: RAR_EMISMATCH).  P == 0 is a no-op. */
+rar_status rar_allreduce_mean(rar_plan_t plan, void *const bufs[], int64_t P, void *stream);
+
+/* As rar_allreduce_mean, then the synchronous SGD step on the binary32
+ * weights w (device, P floats, must not overlap any buffer):
+ * w[e] = w[e] - lr * mean[e] ([Gibiansky] §The communication problem;
+ * [TrainMGPU] §Training Process, step 3; [DDPpage] §DDP). */
+rar_status rar_allreduce_sgd(rar_plan_t plan, void *const bufs[], float *w, float lr, int64_t P,
+                             void *stream);
+
+/* Scatter-reduce with the owner's update, then an all-gather of weights (the
+ * sharded shape of [DDPpage] §FSDP: gradients are reduce-scattered and each
+ * rank updates only the part it owns).  After the call:
+ *   - the owner of chunk c, (c-1) mod N, holds mean[C_c] in bufs[owner][C_c];
+ *     other parts of the gradient buffers hold ring partial sums (unspecified);
+ *   - every weight replica w_reps[n] (device, P floats each) holds
+ *     w_reps[owner][e] - lr*mean[e] for every element e, i.e. the same bits
+ *     rar_allreduce_sgd gives when all replicas start equal.
+ * Only RAR_F32 plans; the algorithm selected by set_algo is ignored (this
+ * call is always the ring: N-1 scatter-reduce steps, N-1 all-gather steps). */
+rar_status rar_reduce_scatter_sgd_allgather(rar_plan_t plan, void *const bufs[],
+                                            float *const w_reps[], float lr, int64_t P,
+                                            void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Buckets: a ragged list of per-layer gradients reduced in fixed-size     */
+/* buckets ([Gibiansky] §Applying allreduce to deep learning: the          */
+/* all-reduce can run on a subset of the parameters, and output-layer      */
+/* gradients are ready first).                                             */
+/* ---------------------------------------------------------------------- */
+
+/* Lay n_tensors tensors (numel[t] elements each, listed in the order
+ * back-propagation produces them) end to end and cut the stream into
+ * buckets of bucket_bytes / sizeof(dtype) elements; a tensor that crosses a
+ * boundary is split.  Host memory only. */
+rar_status rar_bucket_plan(int n_tensors, const int64_t numel[], rar_dtype dtype, int64_t bucket_bytes,
+                           rar_buckets_t *out);
+
+rar_status rar_bucket_destroy(rar_buckets_t b);
+
+/* Number of buckets and the largest bucket's element count. */
+rar_status rar_bucket_count(rar_buckets_t b, int *n_buckets, int64_t *max_bucket_elems);
+
+/* Bucket `bucket`: its first element in the concatenated stream, its element
+ * count and its number of segments.  Any output may be NULL. */
+rar_status rar_bucket_info(rar_buckets_t b, int bucket, int64_t *stream_offset, int64_t *elems,
+                           int *n_segments);
+
+/* Segment `seg` of a bucket: tensor index, offset inside that tensor, offset
+ * inside the bucket, length (elements).  Any output may be NULL. */
+rar_status rar_bucket_segment(rar_buckets_t b, int bucket, int seg, int *tensor, int64_t *tensor_offset,
+                              int64_t *bucket_offset, int64_t *length);
+
+/* Copy the bucket's segments of every rank's tensors into bucket_bufs[n]
+ * (device, >= the bucket's elements).  tensors is a host array of N*n_tensors
+ * device pointers, rank-major: tensors[n*n_tensors + t]. */
+rar_status rar_bucket_pack(rar_buckets_t b, int bucket, int N, void *const tensors[],
+                           void *const bucket_bufs[], void *stream);
+
+/* The reverse copy, from bucket_bufs[n] back into the tensors. */
+rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void *const bucket_bufs[],
+                             void *const tensors[], void *stream);
+
+/* Every bucket in order: pack, all-reduce-mean (plan built inside for the
+ * bucket's size with `chunking` and `algo`), unpack.  bucket_bufs[n] are N
+ * device buffers of at least max_bucket_elems elements, reused by every
+ * bucket.  Element e of a bucket ends bit-identical to what
+ * rar_allreduce_mean gives for that bucket alone. */
+rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
+                                     void *const tensors[], void *const bucket_bufs[], void *stream);
+
+/* ---------------------------------------------------------------------- */
+
+/* Static description of a status code; never NULL. */
+const char *rar_strerror(rar_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int rar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAR_H */

@@ -1,0 +1,225 @@
+"""Python binding of librar.so: one function per C entry point, same names.
+
+Argument marshalling only -- every step of the all-reduce runs in the HIP
+library.  Device buffers may be given as torch tensors (contiguous, on the
+GPU) or as integer device addresses.  ``stream`` may be a torch stream, an
+integer hipStream_t, or None for torch's current stream on the current
+device (the default stream when torch has no GPU).
+
+Status codes other than RAR_OK raise RarError carrying the code.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Sequence
+
+from ._lib import lib
+
+# enums of rar.h
+F32, BF16 = 0, 1
+BALANCED, CEIL, ALIGN16 = 0, 1, 2
+FUSED, RING, NAIVE = 0, 1, 2
+OK, EINVAL, EMISMATCH, EALIGN, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
+MAX_RANKS = 64
+
+
+class RarError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {rar_strerror(status)} ({status})")
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != OK:
+        raise RarError(rc, where)
+
+
+def rar_strerror(status: int) -> str:
+    return lib().rar_strerror(int(status)).decode()
+
+
+def rar_version() -> int:
+    return int(lib().rar_version())
+
+
+def _addr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if not x.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+        if x.numel() and not x.is_cuda:
+            raise ValueError("tensor must be on the GPU")
+        return int(x.data_ptr())
+    raise TypeError(f"not a device buffer: {type(x)!r}")
+
+
+def _ptr_array(xs: Sequence) -> ctypes.Array:
+    arr = (ctypes.c_void_p * max(len(xs), 1))()
+    for i, x in enumerate(xs):
+        arr[i] = _addr(x) or None
+    return arr
+
+
+def _stream(s) -> int:
+    if s is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return int(torch.cuda.current_stream().cuda_stream)
+        except ImportError:
+            pass
+        return 0
+    if isinstance(s, int):
+        return s
+    if hasattr(s, "cuda_stream"):
+        return int(s.cuda_stream)
+    raise TypeError(f"not a stream: {type(s)!r}")
+
+
+# ---------------------------------------------------------------------------
+# Plans
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Owner of a rar_plan_t; destroyed with the object or by rar_plan_destroy."""
+
+    def __init__(self, handle: int, N: int, P: int, dtype: int, chunking: int):
+        self.handle = ctypes.c_void_p(handle)
+        self.N, self.P, self.dtype, self.chunking = N, P, dtype, chunking
+
+    def __del__(self):
+        try:
+            rar_plan_destroy(self)
+        except Exception:
+            pass
+
+
+def rar_plan(N: int, P: int, dtype: int = F32, chunking: int = BALANCED) -> Plan:
+    out = ctypes.c_void_p()
+    _check(lib().rar_plan(int(N), int(P), int(dtype), int(chunking), ctypes.byref(out)), "rar_plan")
+    return Plan(out.value, int(N), int(P), int(dtype), int(chunking))
+
+
+def rar_plan_destroy(plan: Plan) -> None:
+    if plan.handle:
+        h, plan.handle = plan.handle, ctypes.c_void_p()
+        _check(lib().rar_plan_destroy(h), "rar_plan_destroy")
+
+
+def rar_plan_set_algo(plan: Plan, algo: int) -> None:
+    _check(lib().rar_plan_set_algo(plan.handle, int(algo)), "rar_plan_set_algo")
+
+
+def rar_plan_set_grid(plan: Plan, max_blocks: int) -> None:
+    _check(lib().rar_plan_set_grid(plan.handle, int(max_blocks)), "rar_plan_set_grid")
+
+
+def rar_plan_chunk(plan: Plan, c: int):
+    off, ln, own = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int()
+    _check(lib().rar_plan_chunk(plan.handle, int(c), ctypes.byref(off), ctypes.byref(ln), ctypes.byref(own)),
+           "rar_plan_chunk")
+    return off.value, ln.value, own.value
+
+
+def rar_plan_traffic(plan: Plan, rank: int):
+    s, r = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().rar_plan_traffic(plan.handle, int(rank), ctypes.byref(s), ctypes.byref(r)), "rar_plan_traffic")
+    return s.value, r.value
+
+
+# ---------------------------------------------------------------------------
+# All-reduce
+# ---------------------------------------------------------------------------
+
+def rar_allreduce_mean(plan: Plan, bufs: Sequence, P: int, stream=None) -> None:
+    _check(lib().rar_allreduce_mean(plan.handle, _ptr_array(bufs), int(P), _stream(stream)),
+           "rar_allreduce_mean")
+
+
+def rar_allreduce_sgd(plan: Plan, bufs: Sequence, w, lr: float, P: int, stream=None) -> None:
+    _check(lib().rar_allreduce_sgd(plan.handle, _ptr_array(bufs), _addr(w), ctypes.c_float(lr), int(P),
+                                   _stream(stream)), "rar_allreduce_sgd")
+
+
+def rar_reduce_scatter_sgd_allgather(plan: Plan, bufs: Sequence, w_reps: Sequence, lr: float, P: int,
+                                     stream=None) -> None:
+    _check(lib().rar_reduce_scatter_sgd_allgather(plan.handle, _ptr_array(bufs), _ptr_array(w_reps),
+                                                  ctypes.c_float(lr), int(P), _stream(stream)),
+           "rar_reduce_scatter_sgd_allgather")
+
+
+# ---------------------------------------------------------------------------
+# Buckets
+# ---------------------------------------------------------------------------
+
+class Buckets:
+    def __init__(self, handle: int, n_tensors: int, dtype: int):
+        self.handle = ctypes.c_void_p(handle)
+        self.n_tensors, self.dtype = n_tensors, dtype
+
+    def __del__(self):
+        try:
+            rar_bucket_destroy(self)
+        except Exception:
+            pass
+
+
+def rar_bucket_plan(numel: Sequence[int], dtype: int = F32, bucket_bytes: int = 25_000_000) -> Buckets:
+    arr = (ctypes.c_int64 * max(len(numel), 1))(*[int(n) for n in numel])
+    out = ctypes.c_void_p()
+    _check(lib().rar_bucket_plan(len(numel), arr, int(dtype), int(bucket_bytes), ctypes.byref(out)),
+           "rar_bucket_plan")
+    return Buckets(out.value, len(numel), int(dtype))
+
+
+def rar_bucket_destroy(b: Buckets) -> None:
+    if b.handle:
+        h, b.handle = b.handle, ctypes.c_void_p()
+        _check(lib().rar_bucket_destroy(h), "rar_bucket_destroy")
+
+
+def rar_bucket_count(b: Buckets):
+    n, m = ctypes.c_int(), ctypes.c_int64()
+    _check(lib().rar_bucket_count(b.handle, ctypes.byref(n), ctypes.byref(m)), "rar_bucket_count")
+    return n.value, m.value
+
+
+def rar_bucket_info(b: Buckets, bucket: int):
+    so, el, ns = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int()
+    _check(lib().rar_bucket_info(b.handle, int(bucket), ctypes.byref(so), ctypes.byref(el), ctypes.byref(ns)),
+           "rar_bucket_info")
+    return so.value, el.value, ns.value
+
+
+def rar_bucket_segment(b: Buckets, bucket: int, seg: int):
+    t, to, bo, ln = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().rar_bucket_segment(b.handle, int(bucket), int(seg), ctypes.byref(t), ctypes.byref(to),
+                                    ctypes.byref(bo), ctypes.byref(ln)), "rar_bucket_segment")
+    return t.value, to.value, bo.value, ln.value
+
+
+def _rank_major(tensors: Sequence[Sequence]) -> ctypes.Array:
+    flat = [x for rank in tensors for x in rank]
+    return _ptr_array(flat)
+
+
+def rar_bucket_pack(b: Buckets, bucket: int, tensors: Sequence[Sequence], bucket_bufs: Sequence,
+                    stream=None) -> None:
+    _check(lib().rar_bucket_pack(b.handle, int(bucket), len(tensors), _rank_major(tensors),
+                                 _ptr_array(bucket_bufs), _stream(stream)), "rar_bucket_pack")
+
+
+def rar_bucket_unpack(b: Buckets, bucket: int, bucket_bufs: Sequence, tensors: Sequence[Sequence],
+                      stream=None) -> None:
+    _check(lib().rar_bucket_unpack(b.handle, int(bucket), len(tensors), _ptr_array(bucket_bufs),
+                                   _rank_major(tensors), _stream(stream)), "rar_bucket_unpack")
+
+
+def rar_bucket_allreduce_mean(b: Buckets, tensors: Sequence[Sequence], bucket_bufs: Sequence,
+                              chunking: int = BALANCED, algo: int = FUSED, stream=None) -> None:
+    _check(lib().rar_bucket_allreduce_mean(b.handle, len(tensors), int(chunking), int(algo),
+                                           _rank_major(tensors), _ptr_array(bucket_bufs), _stream(stream)),
+           "rar_bucket_allreduce_mean")

@@ -1,0 +1,639 @@
+// rar_host.cpp -- host side of librar.so: plans, argument checks, the launch
+// sequences of each algorithm, and the bucketer.  No device work is enqueued
+// before every argument has been checked.
+//
+// Sources: [Gibiansky] "Bringing HPC Techniques to Deep Learning" (A.
+// Gibiansky, Baidu SVAIL), sections "Scatter-reduce", "Allgather",
+// "Allreduce communication cost", "Applying allreduce to deep learning",
+// "The communication problem"; [DDPpage] "[PyTorch] GPU 분산 학습 1 - DP / DDP
+// / FSDP 개념", sections "DDP" and "FSDP".
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <new>
+#include <tuple>
+#include <vector>
+
+#include "rar_internal.h"
+
+using rar::kMaxRanks;
+
+struct rar_plan_s {
+    int N = 0;
+    int64_t P = 0;
+    rar_dtype dtype = RAR_F32;
+    rar_chunking chunking = RAR_CHUNK_BALANCED;
+    rar_algo algo = RAR_ALGO_FUSED;
+    int max_blocks = 0;          // 0: default
+    rar::ChunkTable ct{};
+    int64_t max_chunk = 0;
+    float *ws = nullptr;         // bf16 ring: binary32 chunk-indexed partial sums
+};
+
+namespace {
+
+constexpr int kDefaultBlocks = 2048;  // 256 CUs x 8 workgroups of 256 lanes
+
+int elem_bytes(rar_dtype d) { return d == RAR_BF16 ? 2 : 4; }
+
+bool valid_dtype(int d) { return d == RAR_F32 || d == RAR_BF16; }
+
+// Chunk table per rar_chunking (see rar.h).
+void cut_chunks(int N, int64_t P, rar_chunking mode, int es, rar::ChunkTable &ct)
+{
+    if (mode == RAR_CHUNK_BALANCED) {
+        const int64_t q = P / N, r = P % N;
+        for (int c = 0; c <= N; ++c)
+            ct.off[c] = c * q + std::min<int64_t>(c, r);
+        return;
+    }
+    int64_t len = (P + N - 1) / N;
+    if (mode == RAR_CHUNK_ALIGN16) {
+        const int64_t g = 16 / es;
+        len = (len + g - 1) / g * g;
+    }
+    for (int c = 0; c < N; ++c)
+        ct.off[c] = std::min<int64_t>(c * len, P);
+    ct.off[N] = P;
+}
+
+int block_budget(const rar_plan_s *pl) { return pl->max_blocks > 0 ? pl->max_blocks : kDefaultBlocks; }
+
+rar_status hip_status(hipError_t e) { return e == hipSuccess ? RAR_OK : RAR_EHIP; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Checks shared by every execute call.  P == 0 returns RAR_OK early through
+// *noop without looking at the pointers (empty tensors may have none).
+rar_status check_exec(const rar_plan_s *pl, void *const bufs[], int64_t P, bool *noop)
+{
+    *noop = false;
+    if (!pl || !bufs)
+        return RAR_EINVAL;
+    if (P != pl->P)
+        return RAR_EMISMATCH;
+    if (P == 0) {
+        *noop = true;
+        return RAR_OK;
+    }
+    const uintptr_t bytes = (uintptr_t)P * elem_bytes(pl->dtype);
+    for (int n = 0; n < pl->N; ++n) {
+        if (!bufs[n])
+            return RAR_EINVAL;
+        if ((uintptr_t)bufs[n] & 15)
+            return RAR_EALIGN;
+    }
+    for (int i = 0; i < pl->N; ++i)
+        for (int j = i + 1; j < pl->N; ++j)
+            if (overlaps({(uintptr_t)bufs[i], (uintptr_t)bufs[i] + bytes},
+                         {(uintptr_t)bufs[j], (uintptr_t)bufs[j] + bytes}))
+                return RAR_EINVAL;
+    return RAR_OK;
+}
+
+rar_status check_weights(const rar_plan_s *pl, void *const bufs[], const float *w)
+{
+    if (!w)
+        return RAR_EINVAL;
+    if ((uintptr_t)w & 15)
+        return RAR_EALIGN;
+    const uintptr_t bytes = (uintptr_t)pl->P * elem_bytes(pl->dtype);
+    const Range wr{(uintptr_t)w, (uintptr_t)w + (uintptr_t)pl->P * 4};
+    for (int n = 0; n < pl->N; ++n)
+        if (overlaps(wr, {(uintptr_t)bufs[n], (uintptr_t)bufs[n] + bytes}))
+            return RAR_EINVAL;
+    return RAR_OK;
+}
+
+// --- launch sequences --------------------------------------------------------
+
+rar_status run_fused(const rar_plan_s *pl, void *const bufs[], float *w, float lr, hipStream_t st)
+{
+    rar::FusedParams p{};
+    for (int n = 0; n < pl->N; ++n)
+        p.bufs.p[n] = bufs[n];
+    p.ct = pl->ct;
+    p.w = w;
+    p.lr = lr;
+    p.N = pl->N;
+    return hip_status(rar::launch_fused(pl->dtype, p, block_budget(pl), pl->max_chunk, st));
+}
+
+// All-gather steps ([Gibiansky] §Allgather): at step s chunk c moves from rank
+// (c+s-1) mod N to rank (c+s) mod N, overwriting.  ptrs are the arrays moved
+// (gradient buffers, or weight replicas), es their element size.
+rar_status run_allgather(const rar_plan_s *pl, void *const ptrs[], int es, hipStream_t st)
+{
+    const int N = pl->N;
+    for (int s = 0; s < N - 1; ++s) {
+        rar::CopyParams cp{};
+        cp.unit = es;
+        for (int c = 0; c < N; ++c) {
+            const int src = (c + s - 1 + N) % N, dst = (c + s) % N;
+            const int64_t off = pl->ct.off[c], len = pl->ct.off[c + 1] - off;
+            cp.job[cp.njobs++] = {static_cast<const char *>(ptrs[src]) + off * es,
+                                  static_cast<char *>(ptrs[dst]) + off * es, len * es};
+        }
+        hipError_t e = rar::launch_copy(cp, block_budget(pl), pl->max_chunk * es, st);
+        if (e != hipSuccess)
+            return RAR_EHIP;
+    }
+    return RAR_OK;
+}
+
+// Scatter-reduce steps ([Gibiansky] §Scatter-reduce); the last one divides by
+// N at the owner and, with SGD, updates the owner's chunk of the weights.
+rar_status run_scatter_reduce(const rar_plan_s *pl, void *const bufs[], float *w, float *const wreps[],
+                              float lr, bool sgd, hipStream_t st)
+{
+    const int N = pl->N;
+    rar::StepParams p{};
+    for (int n = 0; n < N; ++n) {
+        p.bufs.p[n] = bufs[n];
+        if (wreps)
+            p.wreps.p[n] = wreps[n];
+    }
+    p.ct = pl->ct;
+    p.w = w;
+    p.ws = pl->ws;
+    p.lr = lr;
+    p.N = N;
+    p.sharded = wreps ? 1 : 0;
+    for (int s = 0; s < N - 1; ++s) {
+        p.s = s;
+        hipError_t e = rar::launch_sr_step(pl->dtype, p, s == 0, s == N - 2, sgd, block_budget(pl),
+                                           pl->max_chunk, st);
+        if (e != hipSuccess)
+            return RAR_EHIP;
+    }
+    return RAR_OK;
+}
+
+rar_status run_ring(const rar_plan_s *pl, void *const bufs[], float *w, float lr, hipStream_t st)
+{
+    if (pl->N == 1)  // no transfers: the mean of one rank is its gradient
+        return run_fused(pl, bufs, w, lr, st);
+    rar_status rc = run_scatter_reduce(pl, bufs, w, nullptr, lr, w != nullptr, st);
+    if (rc != RAR_OK)
+        return rc;
+    return run_allgather(pl, bufs, elem_bytes(pl->dtype), st);
+}
+
+// Single reducer ([Gibiansky] §The communication problem): rank 0 receives
+// every other rank's gradient in turn, averages, updates, and sends the mean
+// back to every rank.
+rar_status run_naive(const rar_plan_s *pl, void *const bufs[], float *w, float lr, hipStream_t st)
+{
+    const int N = pl->N;
+    if (N == 1)
+        return run_fused(pl, bufs, w, lr, st);
+    rar::PairParams p{};
+    for (int n = 0; n < N; ++n)
+        p.bufs.p[n] = bufs[n];
+    p.w = w;
+    p.lr = lr;
+    p.N = N;
+    p.P = pl->P;
+    for (int src = 1; src < N; ++src) {
+        p.src = src;
+        hipError_t e = rar::launch_pair_add(p, src == N - 1, w != nullptr, block_budget(pl), st);
+        if (e != hipSuccess)
+            return RAR_EHIP;
+    }
+    rar::CopyParams cp{};
+    cp.unit = 4;
+    for (int n = 1; n < N; ++n)
+        cp.job[cp.njobs++] = {bufs[0], bufs[n], pl->P * 4};
+    return hip_status(rar::launch_copy(cp, block_budget(pl), pl->P * 4, st));
+}
+
+rar_status execute(rar_plan_s *pl, void *const bufs[], float *w, float lr, hipStream_t st)
+{
+    switch (pl->algo) {
+    case RAR_ALGO_FUSED: return run_fused(pl, bufs, w, lr, st);
+    case RAR_ALGO_RING: return run_ring(pl, bufs, w, lr, st);
+    case RAR_ALGO_NAIVE: return run_naive(pl, bufs, w, lr, st);
+    }
+    return RAR_EINVAL;
+}
+
+}  // namespace
+
+// =============================================================================
+// Plans
+// =============================================================================
+
+extern "C" rar_status rar_plan(int N, int64_t P, rar_dtype dtype, rar_chunking chunking, rar_plan_t *out)
+{
+    if (!out)
+        return RAR_EINVAL;
+    *out = nullptr;
+    if (N < 1 || N > kMaxRanks || P < 0 || !valid_dtype(dtype))
+        return RAR_EINVAL;
+    if (chunking != RAR_CHUNK_BALANCED && chunking != RAR_CHUNK_CEIL && chunking != RAR_CHUNK_ALIGN16)
+        return RAR_EINVAL;
+    rar_plan_s *pl = new (std::nothrow) rar_plan_s;
+    if (!pl)
+        return RAR_ENOMEM;
+    pl->N = N;
+    pl->P = P;
+    pl->dtype = dtype;
+    pl->chunking = chunking;
+    cut_chunks(N, P, chunking, elem_bytes(dtype), pl->ct);
+    for (int c = 0; c < N; ++c)
+        pl->max_chunk = std::max(pl->max_chunk, pl->ct.off[c + 1] - pl->ct.off[c]);
+    *out = pl;
+    return RAR_OK;
+}
+
+extern "C" rar_status rar_plan_destroy(rar_plan_t plan)
+{
+    if (!plan)
+        return RAR_OK;
+    rar_status rc = RAR_OK;
+    if (plan->ws && hipFree(plan->ws) != hipSuccess)
+        rc = RAR_EHIP;
+    delete plan;
+    return rc;
+}
+
+extern "C" rar_status rar_plan_set_algo(rar_plan_t plan, rar_algo algo)
+{
+    if (!plan)
+        return RAR_EINVAL;
+    if (algo != RAR_ALGO_FUSED && algo != RAR_ALGO_RING && algo != RAR_ALGO_NAIVE)
+        return RAR_EINVAL;
+    if (algo == RAR_ALGO_NAIVE && plan->dtype != RAR_F32)
+        return RAR_EINVAL;
+    if (algo == RAR_ALGO_RING && plan->dtype == RAR_BF16 && !plan->ws && plan->P > 0 && plan->N > 1) {
+        void *p = nullptr;
+        const hipError_t e = hipMalloc(&p, (size_t)plan->P * sizeof(float));
+        if (e == hipErrorOutOfMemory)
+            return RAR_ENOMEM;
+        if (e != hipSuccess)
+            return RAR_EHIP;
+        plan->ws = static_cast<float *>(p);
+    }
+    plan->algo = algo;
+    return RAR_OK;
+}
+
+extern "C" rar_status rar_plan_set_grid(rar_plan_t plan, int max_blocks)
+{
+    if (!plan || max_blocks < 0)
+        return RAR_EINVAL;
+    plan->max_blocks = max_blocks;
+    return RAR_OK;
+}
+
+extern "C" rar_status rar_plan_chunk(rar_plan_t plan, int c, int64_t *offset, int64_t *length, int *owner_rank)
+{
+    if (!plan || c < 0 || c >= plan->N)
+        return RAR_EINVAL;
+    if (offset)
+        *offset = plan->ct.off[c];
+    if (length)
+        *length = plan->ct.off[c + 1] - plan->ct.off[c];
+    if (owner_rank)
+        *owner_rank = (c - 1 + plan->N) % plan->N;
+    return RAR_OK;
+}
+
+extern "C" rar_status rar_plan_traffic(rar_plan_t plan, int rank, int64_t *sent_elems, int64_t *recv_elems)
+{
+    if (!plan || rank < 0 || rank >= plan->N)
+        return RAR_EINVAL;
+    const int N = plan->N;
+    int64_t sent = 0, recv = 0;
+    // walk the schedule: scatter-reduce sends chunk (n-s), all-gather (n+1-s);
+    // the rank receives what its left neighbour sends
+    for (int phase = 0; phase < 2; ++phase) {
+        for (int s = 0; s < N - 1; ++s) {
+            const int cs = ((rank + phase - s) % N + N) % N;
+            const int cr = ((rank - 1 + phase - s) % N + N) % N;
+            sent += plan->ct.off[cs + 1] - plan->ct.off[cs];
+            recv += plan->ct.off[cr + 1] - plan->ct.off[cr];
+        }
+    }
+    if (sent_elems)
+        *sent_elems = sent;
+    if (recv_elems)
+        *recv_elems = recv;
+    return RAR_OK;
+}
+
+// =============================================================================
+// All-reduce
+// =============================================================================
+
+extern "C" rar_status rar_allreduce_mean(rar_plan_t plan, void *const bufs[], int64_t P, void *stream)
+{
+    bool noop;
+    rar_status rc = check_exec(plan, bufs, P, &noop);
+    if (rc != RAR_OK || noop)
+        return rc;
+    return execute(plan, bufs, nullptr, 0.0f, static_cast<hipStream_t>(stream));
+}
+
+extern "C" rar_status rar_allreduce_sgd(rar_plan_t plan, void *const bufs[], float *w, float lr, int64_t P,
+                                        void *stream)
+{
+    bool noop;
+    rar_status rc = check_exec(plan, bufs, P, &noop);
+    if (rc != RAR_OK || noop)
+        return rc;
+    rc = check_weights(plan, bufs, w);
+    if (rc != RAR_OK)
+        return rc;
+    return execute(plan, bufs, w, lr, static_cast<hipStream_t>(stream));
+}
+
+extern "C" rar_status rar_reduce_scatter_sgd_allgather(rar_plan_t plan, void *const bufs[],
+                                                       float *const w_reps[], float lr, int64_t P,
+                                                       void *stream)
+{
+    bool noop;
+    rar_status rc = check_exec(plan, bufs, P, &noop);
+    if (rc != RAR_OK || noop)
+        return rc;
+    if (plan->dtype != RAR_F32 || !w_reps)
+        return RAR_EINVAL;
+    for (int n = 0; n < plan->N; ++n) {
+        rc = check_weights(plan, bufs, w_reps[n]);
+        if (rc != RAR_OK)
+            return rc;
+        const Range a{(uintptr_t)w_reps[n], (uintptr_t)w_reps[n] + (uintptr_t)P * 4};
+        for (int m = 0; m < n; ++m)
+            if (overlaps(a, {(uintptr_t)w_reps[m], (uintptr_t)w_reps[m] + (uintptr_t)P * 4}))
+                return RAR_EINVAL;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (plan->N == 1)
+        return run_fused(plan, bufs, w_reps[0], lr, st);
+    rc = run_scatter_reduce(plan, bufs, nullptr, w_reps, lr, true, st);
+    if (rc != RAR_OK)
+        return rc;
+    return run_allgather(plan, reinterpret_cast<void *const *>(w_reps), 4, st);
+}
+
+// =============================================================================
+// Buckets ([Gibiansky] §Applying allreduce to deep learning)
+// =============================================================================
+
+namespace {
+struct Segment {
+    int tensor;
+    int64_t toff, boff, len;
+};
+}  // namespace
+
+struct rar_buckets_s {
+    rar_dtype dtype = RAR_F32;
+    int n_tensors = 0;
+    int64_t per_bucket = 0;
+    std::vector<int64_t> start, elems;
+    std::vector<std::vector<Segment>> segs;
+    int64_t max_elems = 0;
+    std::mutex mu;  // guards the plan cache
+    std::map<std::tuple<int, int64_t, int, int>, rar_plan_t> plans;
+    ~rar_buckets_s()
+    {
+        for (auto &kv : plans)
+            rar_plan_destroy(kv.second);
+    }
+};
+
+extern "C" rar_status rar_bucket_plan(int n_tensors, const int64_t numel[], rar_dtype dtype, int64_t bucket_bytes,
+                                      rar_buckets_t *out)
+{
+    if (!out)
+        return RAR_EINVAL;
+    *out = nullptr;
+    if (n_tensors < 0 || (n_tensors > 0 && !numel) || !valid_dtype(dtype))
+        return RAR_EINVAL;
+    const int64_t B = bucket_bytes / elem_bytes(dtype);
+    if (B <= 0)
+        return RAR_EINVAL;
+    for (int t = 0; t < n_tensors; ++t)
+        if (numel[t] < 0)
+            return RAR_EINVAL;
+    rar_buckets_s *b = new (std::nothrow) rar_buckets_s;
+    if (!b)
+        return RAR_ENOMEM;
+    b->dtype = dtype;
+    b->n_tensors = n_tensors;
+    b->per_bucket = B;
+    int64_t stream_pos = 0, fill = 0;
+    std::vector<Segment> cur;
+    auto close = [&]() {
+        b->start.push_back(stream_pos - fill);
+        b->elems.push_back(fill);
+        b->max_elems = std::max(b->max_elems, fill);
+        b->segs.push_back(std::move(cur));
+        cur.clear();
+        fill = 0;
+    };
+    for (int t = 0; t < n_tensors; ++t) {
+        int64_t done = 0;
+        while (done < numel[t]) {
+            const int64_t take = std::min(numel[t] - done, B - fill);
+            cur.push_back({t, done, fill, take});
+            done += take;
+            fill += take;
+            stream_pos += take;
+            if (fill == B)
+                close();
+        }
+    }
+    if (fill > 0)
+        close();
+    *out = b;
+    return RAR_OK;
+}
+
+extern "C" rar_status rar_bucket_destroy(rar_buckets_t b)
+{
+    delete b;
+    return RAR_OK;
+}
+
+extern "C" rar_status rar_bucket_count(rar_buckets_t b, int *n_buckets, int64_t *max_bucket_elems)
+{
+    if (!b)
+        return RAR_EINVAL;
+    if (n_buckets)
+        *n_buckets = (int)b->segs.size();
+    if (max_bucket_elems)
+        *max_bucket_elems = b->max_elems;
+    return RAR_OK;
+}
+
+extern "C" rar_status rar_bucket_info(rar_buckets_t b, int bucket, int64_t *stream_offset, int64_t *elems,
+                                      int *n_segments)
+{
+    if (!b || bucket < 0 || bucket >= (int)b->segs.size())
+        return RAR_EINVAL;
+    if (stream_offset)
+        *stream_offset = b->start[bucket];
+    if (elems)
+        *elems = b->elems[bucket];
+    if (n_segments)
+        *n_segments = (int)b->segs[bucket].size();
+    return RAR_OK;
+}
+
+extern "C" rar_status rar_bucket_segment(rar_buckets_t b, int bucket, int seg, int *tensor, int64_t *tensor_offset,
+                                         int64_t *bucket_offset, int64_t *length)
+{
+    if (!b || bucket < 0 || bucket >= (int)b->segs.size() || seg < 0 || seg >= (int)b->segs[bucket].size())
+        return RAR_EINVAL;
+    const Segment &s = b->segs[bucket][seg];
+    if (tensor)
+        *tensor = s.tensor;
+    if (tensor_offset)
+        *tensor_offset = s.toff;
+    if (bucket_offset)
+        *bucket_offset = s.boff;
+    if (length)
+        *length = s.len;
+    return RAR_OK;
+}
+
+namespace {
+
+rar_status check_bucket_args(rar_buckets_t b, int bucket, int N, void *const tensors[], void *const bucket_bufs[])
+{
+    if (!b || bucket < 0 || bucket >= (int)b->segs.size() || N < 1 || N > kMaxRanks || !tensors || !bucket_bufs)
+        return RAR_EINVAL;
+    const int es = elem_bytes(b->dtype);
+    for (int n = 0; n < N; ++n) {
+        if (!bucket_bufs[n])
+            return RAR_EINVAL;
+        if ((uintptr_t)bucket_bufs[n] & 15)
+            return RAR_EALIGN;
+        for (const Segment &s : b->segs[bucket]) {
+            const void *t = tensors[(int64_t)n * b->n_tensors + s.tensor];
+            if (!t)
+                return RAR_EINVAL;
+            if ((uintptr_t)t % es)
+                return RAR_EALIGN;
+        }
+    }
+    return RAR_OK;
+}
+
+// pack (to_bucket) or unpack, in launches of at most kMaxCopyJobs segments
+rar_status bucket_copy(rar_buckets_t b, int bucket, int N, void *const tensors[], void *const bucket_bufs[],
+                       bool to_bucket, hipStream_t st)
+{
+    const int es = elem_bytes(b->dtype);
+    rar::CopyParams cp{};
+    cp.unit = es;
+    int64_t max_bytes = 0;
+    auto flush = [&]() -> rar_status {
+        hipError_t e = rar::launch_copy(cp, kDefaultBlocks, max_bytes, st);
+        cp.njobs = 0;
+        max_bytes = 0;
+        return hip_status(e);
+    };
+    for (int n = 0; n < N; ++n) {
+        for (const Segment &s : b->segs[bucket]) {
+            char *t = static_cast<char *>(tensors[(int64_t)n * b->n_tensors + s.tensor]) + s.toff * es;
+            char *k = static_cast<char *>(bucket_bufs[n]) + s.boff * es;
+            cp.job[cp.njobs++] = to_bucket ? rar::CopyJob{t, k, s.len * es} : rar::CopyJob{k, t, s.len * es};
+            max_bytes = std::max(max_bytes, s.len * es);
+            if (cp.njobs == rar::kMaxCopyJobs) {
+                rar_status rc = flush();
+                if (rc != RAR_OK)
+                    return rc;
+            }
+        }
+    }
+    return cp.njobs ? flush() : RAR_OK;
+}
+
+}  // namespace
+
+extern "C" rar_status rar_bucket_pack(rar_buckets_t b, int bucket, int N, void *const tensors[],
+                                      void *const bucket_bufs[], void *stream)
+{
+    rar_status rc = check_bucket_args(b, bucket, N, tensors, bucket_bufs);
+    if (rc != RAR_OK)
+        return rc;
+    return bucket_copy(b, bucket, N, tensors, bucket_bufs, true, static_cast<hipStream_t>(stream));
+}
+
+extern "C" rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void *const bucket_bufs[],
+                                        void *const tensors[], void *stream)
+{
+    rar_status rc = check_bucket_args(b, bucket, N, tensors, bucket_bufs);
+    if (rc != RAR_OK)
+        return rc;
+    return bucket_copy(b, bucket, N, tensors, bucket_bufs, false, static_cast<hipStream_t>(stream));
+}
+
+extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
+                                                void *const tensors[], void *const bucket_bufs[], void *stream)
+{
+    if (!b)
+        return RAR_EINVAL;
+    const int nb = (int)b->segs.size();
+    for (int k = 0; k < nb; ++k) {
+        rar_status rc = check_bucket_args(b, k, N, tensors, bucket_bufs);
+        if (rc != RAR_OK)
+            return rc;
+    }
+    // plans for the distinct bucket sizes, made once and kept with the buckets
+    std::vector<rar_plan_t> plan_of(nb, nullptr);
+    {
+        std::lock_guard<std::mutex> lock(b->mu);
+        for (int k = 0; k < nb; ++k) {
+            auto key = std::make_tuple(N, b->elems[k], (int)chunking, (int)algo);
+            auto it = b->plans.find(key);
+            if (it == b->plans.end()) {
+                rar_plan_t pl = nullptr;
+                rar_status rc = rar_plan(N, b->elems[k], b->dtype, chunking, &pl);
+                if (rc == RAR_OK)
+                    rc = rar_plan_set_algo(pl, algo);
+                if (rc != RAR_OK) {
+                    rar_plan_destroy(pl);
+                    return rc;
+                }
+                it = b->plans.emplace(key, pl).first;
+            }
+            plan_of[k] = it->second;
+        }
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int k = 0; k < nb; ++k) {
+        rar_status rc = bucket_copy(b, k, N, tensors, bucket_bufs, true, st);
+        if (rc == RAR_OK)
+            rc = rar_allreduce_mean(plan_of[k], bucket_bufs, b->elems[k], stream);
+        if (rc == RAR_OK)
+            rc = bucket_copy(b, k, N, tensors, bucket_bufs, false, st);
+        if (rc != RAR_OK)
+            return rc;
+    }
+    return RAR_OK;
+}
+
+// =============================================================================
+
+extern "C" const char *rar_strerror(rar_status s)
+{
+    switch (s) {
+    case RAR_OK: return "success";
+    case RAR_EINVAL: return "invalid argument";
+    case RAR_EMISMATCH: return "element count differs from the plan";
+    case RAR_EALIGN: return "device pointer not 16-byte aligned";
+    case RAR_ENOMEM: return "out of memory";
+    case RAR_EHIP: return "HIP runtime error (see hipGetLastError)";
+    }
+    return "unknown status";
+}
+
+extern "C" int rar_version(void) { return 100; }

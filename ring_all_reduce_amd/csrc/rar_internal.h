@@ -1,0 +1,78 @@
+// rar_internal.h -- declarations shared by the host code (rar_host.cpp) and the
+// kernels (rar_kernels.hip) of librar.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rar.h"
+
+namespace rar {
+
+constexpr int kMaxRanks = RAR_MAX_RANKS;
+constexpr int kThreads = 256;   // workgroup size of every kernel: four 64-wide waves
+constexpr int kMaxCopyJobs = 64;
+
+// Chunk table: chunk c is [off[c], off[c+1]).  Passed to kernels by value in the
+// kernel-argument segment, so a wave-uniform index becomes a scalar load.
+struct ChunkTable {
+    int64_t off[kMaxRanks + 1];
+};
+
+struct RankPtrs {
+    void *p[kMaxRanks];
+};
+
+// Fused single pass: every rank read once, every rank written once.
+struct FusedParams {
+    RankPtrs bufs;
+    ChunkTable ct;
+    float *w;     // nullptr: mean only
+    float lr;
+    int N;
+};
+
+// One ring step, all N chunk transfers of the step in one launch.
+struct StepParams {
+    RankPtrs bufs;
+    RankPtrs wreps;  // per-rank weight replicas (sharded update), else unused
+    ChunkTable ct;
+    float *w;        // shared weights (nullptr: none)
+    float *ws;       // binary32 chunk-indexed workspace (bf16 ring), else nullptr
+    float lr;
+    int N;
+    int s;           // step index within its phase
+    int sharded;     // 1: the owner updates wreps[owner] instead of w
+};
+
+struct CopyJob {
+    const void *src;
+    void *dst;
+    int64_t nbytes;
+};
+
+struct CopyParams {
+    CopyJob job[kMaxCopyJobs];
+    int njobs;
+    int unit;  // element size in bytes (2 or 4) for unaligned remainders
+};
+
+// Single reducer (prior art): rank 0 accumulates rank `src`.
+struct PairParams {
+    RankPtrs bufs;
+    float *w;
+    float lr;
+    int N;
+    int src;
+    int64_t P;
+};
+
+// ---- launchers (rar_kernels.hip); each returns hipSuccess or the launch error
+hipError_t launch_fused(rar_dtype dt, const FusedParams &p, int max_blocks, int64_t max_chunk,
+                        hipStream_t st);
+hipError_t launch_sr_step(rar_dtype dt, const StepParams &p, bool first, bool last, bool sgd,
+                          int max_blocks, int64_t max_chunk, hipStream_t st);
+hipError_t launch_copy(const CopyParams &p, int max_blocks, int64_t max_job_bytes, hipStream_t st);
+hipError_t launch_pair_add(const PairParams &p, bool last, bool sgd, int max_blocks, hipStream_t st);
+
+}  // namespace rar

@@ -1,0 +1,749 @@
+// rar_kernels.hip -- CDNA4 (gfx950) kernels of the ring all-reduce-mean + SGD.
+//
+// Sources: [Gibiansky] "Bringing HPC Techniques to Deep Learning" (A. Gibiansky,
+// Baidu SVAIL), sections "Ring allreduce", "Scatter-reduce", "Allgather",
+// "Allreduce communication cost"; [TrainMGPU] "[AI System] Training With
+// Multiple GPUs", section "Training Process".
+//
+// All N logical ranks live in one device's HBM, so a ring "transfer" from rank
+// n to rank n+1 is a read of rank n's buffer and a write of rank n+1's.  Every
+// kernel here is a streaming pass bound by HBM bandwidth (well under one flop
+// per byte): there is no contraction and so no MFMA.  What matters is that
+// every byte moves once in 16-byte (dwordx4) accesses that coalesce into whole
+// cache lines, with enough loads in flight per CU to cover HBM latency, and
+// that nothing is re-read.
+//
+// Work decomposition, shared by every kernel: blockIdx.y selects a job (a
+// chunk of the chunk table, or a copy segment); blockIdx.x and a grid-stride
+// loop walk that job's element range.  The 16-byte aligned body of the range
+// is processed in tiles of kThreads*VPT vectors, lane-contiguous so that one
+// wave instruction touches 1 KiB of consecutive memory; the at most VEC-1
+// elements before the first aligned group (the head) and after the last (the
+// tail) go through a scalar path on block 0's first lanes.  Chunk boundaries
+// need not be 16-byte aligned (a balanced cut of P = 1,000,003 over 4 ranks
+// puts them at 250,001 and 500,002), so the per-chunk span keeps a dwordx4
+// access from ever straddling two chunks whose sums start at different ranks.
+//
+// Numerics, identical in every kernel: binary32 adds in ring order starting at
+// the chunk's own rank, one IEEE division by N, SGD as w - (lr*m) with both
+// operations rounded (contraction is off, see the pragma), subnormals kept.
+#include <type_traits>
+
+#include "rar_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace rar {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming accesses: the data are touched once per call, so keep them from
+// displacing other lines in L2 and the Infinity Cache.
+template <typename V>
+__device__ __forceinline__ V ld(const V *p)
+{
+    return __builtin_nontemporal_load(p);
+}
+
+template <typename V>
+__device__ __forceinline__ void st(V *p, V v)
+{
+    __builtin_nontemporal_store(v, p);
+}
+
+__device__ __forceinline__ int next_rank(int r, int N)
+{
+    return (r + 1 == N) ? 0 : r + 1;
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16: the upper 16 bits of a binary32 pattern.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_one(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round to nearest bfloat16, ties to the even pattern: adding 0x7fff plus the
+// lowest kept bit carries into the kept half exactly when the dropped half is
+// above one half, or equal to it with an odd kept half.  NaN: keep sign and
+// leading payload, set the quiet bit.
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void widen8(u32x4 u, f32x4 &a, f32x4 &b)
+{
+    a = f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+    b = f32x4{bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+}
+
+__device__ __forceinline__ u32x4 narrow8(f32x4 a, f32x4 b)
+{
+    return u32x4{bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16),
+                 bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
+}
+
+// ---------------------------------------------------------------------------
+// Span driver
+// ---------------------------------------------------------------------------
+
+// Walk elements [e0, e1) of one job: scalar head and tail on block 0, then the
+// aligned body in tiles (grid-stride over blockIdx.x).  VEC = elements per
+// 16 bytes.  elem(e) handles one element; tile(FULL, a0, v0, nvec) handles
+// vectors v0 .. v0+kThreads*VPT-1 of the body that starts at element a0
+// (lane-contiguous), bounds-checked against nvec unless FULL.
+template <int VEC, int VPT, class ElemF, class TileF>
+__device__ __forceinline__ void run_span(int64_t e0, int64_t e1, ElemF &&elem, TileF &&tile)
+{
+    if (e1 <= e0)
+        return;
+    int64_t a0 = (e0 + VEC - 1) / VEC * VEC;
+    int64_t a1 = e1 / VEC * VEC;
+    if (a0 > a1) {  // the whole span sits inside one 16-byte group
+        a0 = e1;
+        a1 = e1;
+    }
+    if (blockIdx.x == 0) {
+        const int t = threadIdx.x;
+        if (t < a0 - e0)
+            elem(e0 + t);
+        else if (t >= VEC && t < VEC + (e1 - a1))
+            elem(a1 + (t - VEC));
+    }
+    const int64_t nvec = (a1 - a0) / VEC;
+    constexpr int64_t TV = (int64_t)kThreads * VPT;
+    const int64_t ntiles = (nvec + TV - 1) / TV;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t v0 = t * TV;
+        if (v0 + TV <= nvec)
+            tile(std::true_type{}, a0, v0, nvec);
+        else
+            tile(std::false_type{}, a0, v0, nvec);
+    }
+}
+
+template <int VPT, bool FULL>
+__device__ __forceinline__ void lane_vectors(int64_t v0, int64_t nvec, int64_t (&vi)[VPT], bool (&ok)[VPT])
+{
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        vi[j] = v0 + (int64_t)j * kThreads + threadIdx.x;
+        ok[j] = FULL || vi[j] < nvec;
+    }
+}
+
+template <typename V, typename T>
+__device__ __forceinline__ V *vec_at(void *base, int64_t a0)
+{
+    return reinterpret_cast<V *>(static_cast<T *>(base) + a0);
+}
+
+// ---------------------------------------------------------------------------
+// Fused single pass, binary32.
+// ---------------------------------------------------------------------------
+//
+// Chunk c = blockIdx.y.  Each lane loads its vectors from ranks c, c+1, ...,
+// c+N-1 (mod N) -- the order in which the scatter-reduce of [Gibiansky] folds
+// chunk c -- adds them in that order, divides by N, stores the mean into all
+// N buffers and, with SGD, updates w.  N compile-time (NT > 0) lets all N-1
+// loads of a tile be in flight before the first add; NT == 0 takes N from the
+// arguments and keeps KB loads in flight.
+
+template <int NT, int VPT, bool SGD>
+__global__ __launch_bounds__(kThreads) void rar_fused_f32(FusedParams p)
+{
+    const int N = NT > 0 ? NT : p.N;
+    const int c = blockIdx.y;
+    constexpr int KB = NT > 0 ? (NT > 1 ? NT - 1 : 1) : 8;
+
+    auto elem = [&](int64_t e) {
+        float acc = static_cast<const float *>(p.bufs.p[c])[e];
+        int r = c;
+        for (int k = 1; k < N; ++k) {
+            r = next_rank(r, N);
+            acc = acc + static_cast<const float *>(p.bufs.p[r])[e];
+        }
+        const float m = acc / (float)N;
+        for (int n = 0; n < N; ++n)
+            static_cast<float *>(p.bufs.p[n])[e] = m;
+        if (SGD) {
+            const float step = p.lr * m;
+            p.w[e] = p.w[e] - step;
+        }
+    };
+
+    auto tile = [&](auto full, int64_t a0, int64_t v0, int64_t nvec) {
+        constexpr bool FULL = decltype(full)::value;
+        int64_t vi[VPT];
+        bool ok[VPT];
+        lane_vectors<VPT, FULL>(v0, nvec, vi, ok);
+        f32x4 acc[VPT];
+        {
+            const f32x4 *src = vec_at<const f32x4, const float>(p.bufs.p[c], a0);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j)
+                if (ok[j])
+                    acc[j] = ld(src + vi[j]);
+        }
+        int r = c;
+        for (int k = 1; k < N; k += KB) {
+            f32x4 x[KB][VPT];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                if (NT > 0 || k + kk < N) {
+                    r = next_rank(r, N);
+                    const f32x4 *src = vec_at<const f32x4, const float>(p.bufs.p[r], a0);
+#pragma unroll
+                    for (int j = 0; j < VPT; ++j)
+                        if (ok[j])
+                            x[kk][j] = ld(src + vi[j]);
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                if (NT > 0 || k + kk < N) {
+#pragma unroll
+                    for (int j = 0; j < VPT; ++j)
+                        if (ok[j])
+                            acc[j] = acc[j] + x[kk][j];
+                }
+            }
+        }
+        const float fN = (float)N;
+        f32x4 m[VPT];
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+            m[j] = acc[j] / fN;
+        for (int n = 0; n < N; ++n) {
+            f32x4 *dst = vec_at<f32x4, float>(p.bufs.p[n], a0);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j)
+                if (ok[j])
+                    st(dst + vi[j], m[j]);
+        }
+        if (SGD) {
+            f32x4 *wp = vec_at<f32x4, float>(p.w, a0);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                if (ok[j]) {
+                    f32x4 wv = ld(wp + vi[j]);
+                    const f32x4 step = p.lr * m[j];
+                    wv = wv - step;
+                    st(wp + vi[j], wv);
+                }
+            }
+        }
+    };
+
+    run_span<4, VPT>(p.ct.off[c], p.ct.off[c + 1], elem, tile);
+}
+
+// ---------------------------------------------------------------------------
+// Fused single pass, bfloat16 storage with binary32 arithmetic.
+// ---------------------------------------------------------------------------
+
+template <int NT, bool SGD>
+__global__ __launch_bounds__(kThreads) void rar_fused_bf16(FusedParams p)
+{
+    constexpr int VPT = 1;
+    const int N = NT > 0 ? NT : p.N;
+    const int c = blockIdx.y;
+    constexpr int KB = NT > 0 ? (NT > 1 ? NT - 1 : 1) : 8;
+
+    auto elem = [&](int64_t e) {
+        float acc = bf16_one(static_cast<const uint16_t *>(p.bufs.p[c])[e]);
+        int r = c;
+        for (int k = 1; k < N; ++k) {
+            r = next_rank(r, N);
+            acc = acc + bf16_one(static_cast<const uint16_t *>(p.bufs.p[r])[e]);
+        }
+        const float m = acc / (float)N;
+        const uint16_t h = (uint16_t)bf16_rne(m);
+        for (int n = 0; n < N; ++n)
+            static_cast<uint16_t *>(p.bufs.p[n])[e] = h;
+        if (SGD) {
+            const float step = p.lr * m;
+            p.w[e] = p.w[e] - step;
+        }
+    };
+
+    auto tile = [&](auto full, int64_t a0, int64_t v0, int64_t nvec) {
+        constexpr bool FULL = decltype(full)::value;
+        int64_t vi[VPT];
+        bool ok[VPT];
+        lane_vectors<VPT, FULL>(v0, nvec, vi, ok);
+        f32x4 lo[VPT], hi[VPT];
+        {
+            const u32x4 *src = vec_at<const u32x4, const uint16_t>(p.bufs.p[c], a0);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j)
+                if (ok[j])
+                    widen8(ld(src + vi[j]), lo[j], hi[j]);
+        }
+        int r = c;
+        for (int k = 1; k < N; k += KB) {
+            u32x4 x[KB][VPT];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                if (NT > 0 || k + kk < N) {
+                    r = next_rank(r, N);
+                    const u32x4 *src = vec_at<const u32x4, const uint16_t>(p.bufs.p[r], a0);
+#pragma unroll
+                    for (int j = 0; j < VPT; ++j)
+                        if (ok[j])
+                            x[kk][j] = ld(src + vi[j]);
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                if (NT > 0 || k + kk < N) {
+#pragma unroll
+                    for (int j = 0; j < VPT; ++j) {
+                        if (ok[j]) {
+                            f32x4 a, b;
+                            widen8(x[kk][j], a, b);
+                            lo[j] = lo[j] + a;
+                            hi[j] = hi[j] + b;
+                        }
+                    }
+                }
+            }
+        }
+        const float fN = (float)N;
+        f32x4 mlo[VPT], mhi[VPT];
+        u32x4 out[VPT];
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            mlo[j] = lo[j] / fN;
+            mhi[j] = hi[j] / fN;
+            out[j] = narrow8(mlo[j], mhi[j]);
+        }
+        for (int n = 0; n < N; ++n) {
+            u32x4 *dst = vec_at<u32x4, uint16_t>(p.bufs.p[n], a0);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j)
+                if (ok[j])
+                    st(dst + vi[j], out[j]);
+        }
+        if (SGD) {
+            f32x4 *wp = vec_at<f32x4, float>(p.w, a0);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                if (ok[j]) {
+                    f32x4 w0 = ld(wp + 2 * vi[j]);
+                    f32x4 w1 = ld(wp + 2 * vi[j] + 1);
+                    const f32x4 s0 = p.lr * mlo[j];
+                    const f32x4 s1 = p.lr * mhi[j];
+                    w0 = w0 - s0;
+                    w1 = w1 - s1;
+                    st(wp + 2 * vi[j], w0);
+                    st(wp + 2 * vi[j] + 1, w1);
+                }
+            }
+        }
+    };
+
+    run_span<8, VPT>(p.ct.off[c], p.ct.off[c + 1], elem, tile);
+}
+
+// ---------------------------------------------------------------------------
+// One scatter-reduce step, binary32, all N transfers of the step at once.
+// ---------------------------------------------------------------------------
+//
+// [Gibiansky] §Scatter-reduce: at step s rank n sends chunk (n-s) mod N to
+// rank n+1, which adds it into its own copy.  Seen from chunk c: the sender is
+// rank (c+s) mod N and the receiver (c+s+1) mod N.  Within one step no rank
+// reads and writes the same chunk, so the N transfers run concurrently in
+// place.  The last step (s = N-2) completes the sum at the owner (c-1) mod N,
+// which divides by N there and, with SGD, updates the weights of that chunk.
+
+template <int VPT, bool LAST, bool SGD>
+__global__ __launch_bounds__(kThreads) void rar_sr_step_f32(StepParams p)
+{
+    const int N = p.N;
+    const int c = blockIdx.y;
+    const int src = (c + p.s) % N;
+    const int dst = (c + p.s + 1) % N;
+    const float *sp = static_cast<const float *>(p.bufs.p[src]);
+    float *dp = static_cast<float *>(p.bufs.p[dst]);
+    float *w = p.sharded ? static_cast<float *>(p.wreps.p[dst]) : p.w;
+
+    auto elem = [&](int64_t e) {
+        float v = dp[e] + sp[e];
+        if (LAST) {
+            v = v / (float)N;
+            if (SGD) {
+                const float step = p.lr * v;
+                w[e] = w[e] - step;
+            }
+        }
+        dp[e] = v;
+    };
+
+    auto tile = [&](auto full, int64_t a0, int64_t v0, int64_t nvec) {
+        constexpr bool FULL = decltype(full)::value;
+        int64_t vi[VPT];
+        bool ok[VPT];
+        lane_vectors<VPT, FULL>(v0, nvec, vi, ok);
+        const f32x4 *s4 = reinterpret_cast<const f32x4 *>(sp + a0);
+        f32x4 *d4 = reinterpret_cast<f32x4 *>(dp + a0);
+        f32x4 a[VPT], b[VPT];
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            if (ok[j]) {
+                a[j] = ld(d4 + vi[j]);
+                b[j] = ld(s4 + vi[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            if (ok[j]) {
+                f32x4 v = a[j] + b[j];
+                if (LAST) {
+                    v = v / (float)N;
+                    if (SGD) {
+                        f32x4 *w4 = reinterpret_cast<f32x4 *>(w + a0);
+                        f32x4 wv = ld(w4 + vi[j]);
+                        const f32x4 step = p.lr * v;
+                        wv = wv - step;
+                        st(w4 + vi[j], wv);
+                    }
+                }
+                st(d4 + vi[j], v);
+            }
+        }
+    };
+
+    run_span<4, VPT>(p.ct.off[c], p.ct.off[c + 1], elem, tile);
+}
+
+// bf16 scatter-reduce step.  The running partial sum of chunk c travels in the
+// binary32 workspace ws[C_c] (one holder per chunk at any step, so one
+// chunk-indexed array serves all ranks).  FIRST: ws = own + sender's bf16;
+// later: ws = own + ws; LAST: the owner's bf16 chunk receives the rounded
+// mean, and the update uses the binary32 mean.
+template <bool FIRST, bool LAST, bool SGD>
+__global__ __launch_bounds__(kThreads) void rar_sr_step_bf16(StepParams p)
+{
+    constexpr int VPT = 1;
+    const int N = p.N;
+    const int c = blockIdx.y;
+    const int src = (c + p.s) % N;
+    const int dst = (c + p.s + 1) % N;
+    const uint16_t *sp = static_cast<const uint16_t *>(p.bufs.p[src]);
+    uint16_t *dp = static_cast<uint16_t *>(p.bufs.p[dst]);
+    float *ws = p.ws;
+    float *w = p.w;
+
+    auto elem = [&](int64_t e) {
+        const float incoming = FIRST ? bf16_one(sp[e]) : ws[e];
+        const float v = bf16_one(dp[e]) + incoming;
+        if (LAST) {
+            const float m = v / (float)N;
+            dp[e] = (uint16_t)bf16_rne(m);
+            if (SGD) {
+                const float step = p.lr * m;
+                w[e] = w[e] - step;
+            }
+        } else {
+            ws[e] = v;
+        }
+    };
+
+    auto tile = [&](auto full, int64_t a0, int64_t v0, int64_t nvec) {
+        constexpr bool FULL = decltype(full)::value;
+        int64_t vi[VPT];
+        bool ok[VPT];
+        lane_vectors<VPT, FULL>(v0, nvec, vi, ok);
+        if (!ok[0])
+            return;
+        const int64_t v = vi[0];
+        u32x4 *d16 = reinterpret_cast<u32x4 *>(dp + a0);
+        f32x4 *w4 = reinterpret_cast<f32x4 *>(ws + a0);
+        f32x4 olo, ohi, ilo, ihi;
+        widen8(ld(d16 + v), olo, ohi);
+        if (FIRST) {
+            widen8(ld(reinterpret_cast<const u32x4 *>(sp + a0) + v), ilo, ihi);
+        } else {
+            ilo = ld(w4 + 2 * v);
+            ihi = ld(w4 + 2 * v + 1);
+        }
+        f32x4 slo = olo + ilo, shi = ohi + ihi;
+        if (LAST) {
+            slo = slo / (float)N;
+            shi = shi / (float)N;
+            st(d16 + v, narrow8(slo, shi));
+            if (SGD) {
+                f32x4 *wp = reinterpret_cast<f32x4 *>(w + a0);
+                f32x4 w0 = ld(wp + 2 * v), w1 = ld(wp + 2 * v + 1);
+                const f32x4 s0 = p.lr * slo, s1 = p.lr * shi;
+                w0 = w0 - s0;
+                w1 = w1 - s1;
+                st(wp + 2 * v, w0);
+                st(wp + 2 * v + 1, w1);
+            }
+        } else {
+            st(w4 + 2 * v, slo);
+            st(w4 + 2 * v + 1, shi);
+        }
+    };
+
+    run_span<8, VPT>(p.ct.off[c], p.ct.off[c + 1], elem, tile);
+}
+
+// ---------------------------------------------------------------------------
+// Multi-job copy: all-gather steps ([Gibiansky] §Allgather: the receiver
+// overwrites), bucket pack/unpack, and the single reducer's broadcast.
+// ---------------------------------------------------------------------------
+
+template <int VPT>
+__global__ __launch_bounds__(kThreads) void rar_copy(CopyParams p)
+{
+    const CopyJob job = p.job[blockIdx.y];
+    const char *s = static_cast<const char *>(job.src);
+    char *d = static_cast<char *>(job.dst);
+    const int64_t n = job.nbytes;
+    const int unit = p.unit;
+    auto copy_unit = [&](int64_t byte) {
+        if (unit == 4)
+            *reinterpret_cast<uint32_t *>(d + byte) = *reinterpret_cast<const uint32_t *>(s + byte);
+        else
+            *reinterpret_cast<uint16_t *>(d + byte) = *reinterpret_cast<const uint16_t *>(s + byte);
+    };
+    if (n <= 0)
+        return;
+    if ((((uintptr_t)s ^ (uintptr_t)d) & 15) == 0) {
+        // same offset within a 16-byte group: scalar units up to the first
+        // aligned group, dwordx4 body, scalar units after the last group
+        const int64_t head = (int64_t)((16 - ((uintptr_t)d & 15)) & 15) < n
+                                 ? (int64_t)((16 - ((uintptr_t)d & 15)) & 15)
+                                 : n;
+        const int64_t body = (n - head) / 16;
+        const int64_t tail0 = head + body * 16;
+        if (blockIdx.x == 0) {
+            const int64_t t = threadIdx.x;
+            if (t * unit < head)
+                copy_unit(t * unit);
+            else if (t >= 16 && (t - 16) * unit < n - tail0)
+                copy_unit(tail0 + (t - 16) * unit);
+        }
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(s + head);
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(d + head);
+        constexpr int64_t TV = (int64_t)kThreads * VPT;
+        const int64_t ntiles = (body + TV - 1) / TV;
+        for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+            const int64_t v0 = t * TV;
+            u32x4 x[VPT];
+            if (v0 + TV <= body) {
+#pragma unroll
+                for (int j = 0; j < VPT; ++j)
+                    x[j] = ld(s4 + v0 + (int64_t)j * kThreads + threadIdx.x);
+#pragma unroll
+                for (int j = 0; j < VPT; ++j)
+                    st(d4 + v0 + (int64_t)j * kThreads + threadIdx.x, x[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < VPT; ++j) {
+                    const int64_t v = v0 + (int64_t)j * kThreads + threadIdx.x;
+                    if (v < body)
+                        st(d4 + v, ld(s4 + v));
+                }
+            }
+        }
+    } else {
+        const int64_t units = n / unit;
+        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < units;
+             i += (int64_t)gridDim.x * kThreads)
+            copy_unit(i * unit);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Single reducer (prior art): rank 0 adds rank `src`; the last addition also
+// divides by N and applies SGD.  Summation order g0 + g1 + ... + g(N-1).
+// ---------------------------------------------------------------------------
+
+template <int VPT, bool LAST, bool SGD>
+__global__ __launch_bounds__(kThreads) void rar_reduce_into_rank0_f32(PairParams p)
+{
+    const int N = p.N;
+    const float *sp = static_cast<const float *>(p.bufs.p[p.src]);
+    float *dp = static_cast<float *>(p.bufs.p[0]);
+    float *w = p.w;
+    auto elem = [&](int64_t e) {
+        float v = dp[e] + sp[e];
+        if (LAST) {
+            v = v / (float)N;
+            if (SGD) {
+                const float step = p.lr * v;
+                w[e] = w[e] - step;
+            }
+        }
+        dp[e] = v;
+    };
+    auto tile = [&](auto full, int64_t a0, int64_t v0, int64_t nvec) {
+        constexpr bool FULL = decltype(full)::value;
+        int64_t vi[VPT];
+        bool ok[VPT];
+        lane_vectors<VPT, FULL>(v0, nvec, vi, ok);
+        const f32x4 *s4 = reinterpret_cast<const f32x4 *>(sp + a0);
+        f32x4 *d4 = reinterpret_cast<f32x4 *>(dp + a0);
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            if (ok[j]) {
+                f32x4 v = ld(d4 + vi[j]) + ld(s4 + vi[j]);
+                if (LAST) {
+                    v = v / (float)N;
+                    if (SGD) {
+                        f32x4 *w4 = reinterpret_cast<f32x4 *>(w + a0);
+                        f32x4 wv = ld(w4 + vi[j]);
+                        const f32x4 step = p.lr * v;
+                        wv = wv - step;
+                        st(w4 + vi[j], wv);
+                    }
+                }
+                st(d4 + vi[j], v);
+            }
+        }
+    };
+    run_span<4, VPT>(0, p.P, elem, tile);
+}
+
+// ---------------------------------------------------------------------------
+// Launch shapes
+// ---------------------------------------------------------------------------
+
+// Blocks along x for `jobs` jobs of at most `max_vecs` 16-byte vectors each:
+// the plan's block budget split over the jobs, never more than the largest
+// job can use.
+int blocks_x(int max_blocks, int jobs, int64_t max_vecs, int vpt)
+{
+    const int64_t per_tile = (int64_t)kThreads * vpt;
+    int64_t need = (max_vecs + per_tile - 1) / per_tile;
+    if (need < 1)
+        need = 1;
+    int64_t bx = (max_blocks + jobs - 1) / jobs;
+    if (bx < 1)
+        bx = 1;
+    if (bx > need)
+        bx = need;
+    if (bx > 65535)
+        bx = 65535;
+    return (int)bx;
+}
+
+template <int NT>
+hipError_t fused_f32_n(const FusedParams &p, bool sgd, dim3 g, hipStream_t st)
+{
+    constexpr int VPT = (NT > 0 && NT <= 16) ? 2 : 1;
+    if (sgd)
+        hipLaunchKernelGGL((rar_fused_f32<NT, VPT, true>), g, dim3(kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((rar_fused_f32<NT, VPT, false>), g, dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int NT>
+hipError_t fused_bf16_n(const FusedParams &p, bool sgd, dim3 g, hipStream_t st)
+{
+    if (sgd)
+        hipLaunchKernelGGL((rar_fused_bf16<NT, true>), g, dim3(kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((rar_fused_bf16<NT, false>), g, dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fused(rar_dtype dt, const FusedParams &p, int max_blocks, int64_t max_chunk,
+                        hipStream_t st)
+{
+    const bool sgd = p.w != nullptr;
+    if (dt == RAR_F32) {
+        const int vpt = (p.N <= 16) ? 2 : 1;
+        const dim3 g(blocks_x(max_blocks, p.N, max_chunk / 4 + 1, vpt), p.N);
+        switch (p.N) {
+        case 4: return fused_f32_n<4>(p, sgd, g, st);
+        case 8: return fused_f32_n<8>(p, sgd, g, st);
+        case 10: return fused_f32_n<10>(p, sgd, g, st);
+        case 40: return fused_f32_n<40>(p, sgd, g, st);
+        default: {
+            const dim3 g1(blocks_x(max_blocks, p.N, max_chunk / 4 + 1, 1), p.N);
+            return fused_f32_n<0>(p, sgd, g1, st);
+        }
+        }
+    }
+    const dim3 g(blocks_x(max_blocks, p.N, max_chunk / 8 + 1, 1), p.N);
+    switch (p.N) {
+    case 8: return fused_bf16_n<8>(p, sgd, g, st);
+    case 40: return fused_bf16_n<40>(p, sgd, g, st);
+    default: return fused_bf16_n<0>(p, sgd, g, st);
+    }
+}
+
+hipError_t launch_sr_step(rar_dtype dt, const StepParams &p, bool first, bool last, bool sgd,
+                          int max_blocks, int64_t max_chunk, hipStream_t st)
+{
+    const dim3 b(kThreads);
+    if (dt == RAR_F32) {
+        constexpr int VPT = 2;
+        const dim3 g(blocks_x(max_blocks, p.N, max_chunk / 4 + 1, VPT), p.N);
+        if (!last)
+            hipLaunchKernelGGL((rar_sr_step_f32<VPT, false, false>), g, b, 0, st, p);
+        else if (sgd)
+            hipLaunchKernelGGL((rar_sr_step_f32<VPT, true, true>), g, b, 0, st, p);
+        else
+            hipLaunchKernelGGL((rar_sr_step_f32<VPT, true, false>), g, b, 0, st, p);
+        return hipGetLastError();
+    }
+    const dim3 g(blocks_x(max_blocks, p.N, max_chunk / 8 + 1, 1), p.N);
+    if (first && last) {
+        if (sgd)
+            hipLaunchKernelGGL((rar_sr_step_bf16<true, true, true>), g, b, 0, st, p);
+        else
+            hipLaunchKernelGGL((rar_sr_step_bf16<true, true, false>), g, b, 0, st, p);
+    } else if (first) {
+        hipLaunchKernelGGL((rar_sr_step_bf16<true, false, false>), g, b, 0, st, p);
+    } else if (last) {
+        if (sgd)
+            hipLaunchKernelGGL((rar_sr_step_bf16<false, true, true>), g, b, 0, st, p);
+        else
+            hipLaunchKernelGGL((rar_sr_step_bf16<false, true, false>), g, b, 0, st, p);
+    } else {
+        hipLaunchKernelGGL((rar_sr_step_bf16<false, false, false>), g, b, 0, st, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(const CopyParams &p, int max_blocks, int64_t max_job_bytes, hipStream_t st)
+{
+    if (p.njobs <= 0)
+        return hipSuccess;
+    constexpr int VPT = 2;
+    const dim3 g(blocks_x(max_blocks, p.njobs, max_job_bytes / 16 + 1, VPT), p.njobs);
+    hipLaunchKernelGGL((rar_copy<VPT>), g, dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_pair_add(const PairParams &p, bool last, bool sgd, int max_blocks, hipStream_t st)
+{
+    constexpr int VPT = 2;
+    const dim3 g(blocks_x(max_blocks, 1, p.P / 4 + 1, VPT), 1);
+    const dim3 b(kThreads);
+    if (!last)
+        hipLaunchKernelGGL((rar_reduce_into_rank0_f32<VPT, false, false>), g, b, 0, st, p);
+    else if (sgd)
+        hipLaunchKernelGGL((rar_reduce_into_rank0_f32<VPT, true, true>), g, b, 0, st, p);
+    else
+        hipLaunchKernelGGL((rar_reduce_into_rank0_f32<VPT, true, false>), g, b, 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace rar

@@ -1,0 +1,156 @@
+"""The C ABI without a GPU: exports, host-side argument checks, and the host
+tables (chunks, owners, traffic, buckets) against the oracle's independent
+implementation.  No call here reaches a kernel launch: every execute call is
+made with arguments the library must reject first, or with P == 0."""
+import ctypes
+import re
+import pathlib
+
+import numpy as np
+import pytest
+
+import oracle
+from ring_all_reduce_amd import api, synth
+from ring_all_reduce_amd._lib import lib, SIGNATURES
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "rar.h"
+
+
+def _declared():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rar_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = _declared()
+    assert len(names) >= 19
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(SIGNATURES) == names
+
+
+def test_version_and_strerror():
+    assert api.rar_version() >= 100
+    for code in (api.OK, api.EINVAL, api.EMISMATCH, api.EALIGN, api.ENOMEM, api.EHIP, -99):
+        assert isinstance(api.rar_strerror(code), str) and api.rar_strerror(code)
+
+
+@pytest.mark.parametrize("N,P,dt,ch", [(0, 10, 0, 0), (65, 10, 0, 0), (4, -1, 0, 0), (4, 10, 2, 0),
+                                       (4, 10, 0, 3), (-1, 0, 0, 0)])
+def test_plan_rejects_bad_arguments(N, P, dt, ch):
+    with pytest.raises(api.RarError) as e:
+        api.rar_plan(N, P, dt, ch)
+    assert e.value.status == api.EINVAL
+    assert lib().rar_plan(4, 10, 0, 0, None) == api.EINVAL
+
+
+@pytest.mark.parametrize("N,P", [(1, 0), (1, 7), (4, 1_000_003), (10, 11_700_000), (10, 300_000_000),
+                                 (8, 781_250 * 8), (40, 100_000_000), (64, 63), (7, 3), (13, 1000)])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("dt", [0, 1])
+def test_chunk_table_matches_oracle(N, P, mode, dt):
+    eb = 4 if dt == 0 else 2
+    plan = api.rar_plan(N, P, dt, mode)
+    ref = oracle.partition(N, P, mode, eb)
+    for c in range(N):
+        off, ln, own = api.rar_plan_chunk(plan, c)
+        assert (off, ln) == (ref[c], ref[c + 1] - ref[c])
+        assert own == oracle.owner(c, N)
+    with pytest.raises(api.RarError):
+        api.rar_plan_chunk(plan, N)
+    s_ref, r_ref = oracle.ring_traffic(N, ref)
+    for n in range(N):
+        assert api.rar_plan_traffic(plan, n) == (s_ref[n], r_ref[n])
+
+
+def test_traffic_equals_page_formula_when_n_divides_p():
+    N, P = 10, 300_000_000
+    plan = api.rar_plan(N, P)
+    for n in range(N):
+        assert api.rar_plan_traffic(plan, n) == (2 * (N - 1) * P // N,) * 2
+
+
+FAKE = 1 << 40  # never dereferenced: each call below must fail validation first
+
+
+def _fake_bufs(N, P, es=4, gap=None):
+    gap = gap if gap is not None else ((P * es + 4095) // 4096) * 4096 + 4096
+    return [FAKE + i * gap for i in range(N)]
+
+
+def test_execute_rejects_before_touching_the_device():
+    N, P = 4, 1000
+    plan = api.rar_plan(N, P)
+    bufs = _fake_bufs(N, P)
+    L = lib()
+    assert L.rar_allreduce_mean(plan.handle, None, P, None) == api.EINVAL
+    assert L.rar_allreduce_mean(None, api._ptr_array(bufs), P, None) == api.EINVAL
+    assert L.rar_allreduce_mean(plan.handle, api._ptr_array(bufs), P + 1, None) == api.EMISMATCH
+    assert L.rar_allreduce_mean(plan.handle, api._ptr_array(bufs[:3] + [0]), P, None) == api.EINVAL
+    assert L.rar_allreduce_mean(plan.handle, api._ptr_array(bufs[:3] + [bufs[3] + 4]), P, None) == api.EALIGN
+    assert L.rar_allreduce_mean(plan.handle, api._ptr_array(bufs[:3] + [bufs[0]]), P, None) == api.EINVAL
+    overlap = bufs[:3] + [bufs[2] + 16 * ((P * 4) // 32)]
+    assert L.rar_allreduce_mean(plan.handle, api._ptr_array(overlap), P, None) == api.EINVAL
+    f = ctypes.c_float(0.1)
+    assert L.rar_allreduce_sgd(plan.handle, api._ptr_array(bufs), None, f, P, None) == api.EINVAL
+    assert L.rar_allreduce_sgd(plan.handle, api._ptr_array(bufs), bufs[1] + 64, f, P, None) == api.EINVAL
+    assert L.rar_allreduce_sgd(plan.handle, api._ptr_array(bufs), FAKE - 8, f, P, None) == api.EALIGN
+    assert L.rar_reduce_scatter_sgd_allgather(plan.handle, api._ptr_array(bufs), None, f, P, None) == api.EINVAL
+    wdup = api._ptr_array([FAKE + (1 << 36)] * N)
+    assert L.rar_reduce_scatter_sgd_allgather(plan.handle, api._ptr_array(bufs), wdup, f, P, None) == api.EINVAL
+
+
+def test_zero_elements_is_a_no_op():
+    plan = api.rar_plan(3, 0)
+    api.rar_allreduce_mean(plan, [0, 0, 0], 0, stream=0)
+    api.rar_allreduce_sgd(plan, [0, 0, 0], 0, 0.1, 0, stream=0)
+
+
+def test_set_algo_and_grid_checks():
+    plan = api.rar_plan(4, 100, api.BF16)
+    with pytest.raises(api.RarError):
+        api.rar_plan_set_algo(plan, api.NAIVE)
+    with pytest.raises(api.RarError):
+        api.rar_plan_set_algo(plan, 7)
+    with pytest.raises(api.RarError):
+        api.rar_plan_set_grid(plan, -1)
+    f32 = api.rar_plan(4, 100)
+    for a in (api.FUSED, api.RING, api.NAIVE):
+        api.rar_plan_set_algo(f32, a)  # no workspace for binary32: no device call
+    api.rar_plan_set_grid(f32, 17)
+
+
+def test_bucket_layout_matches_oracle():
+    specs = synth.transformer_tensors(12)
+    numels = [s.numel for s in specs]
+    b = api.rar_bucket_plan(numels, api.F32, 25_000_000)
+    ref = oracle.bucket_layout(numels, 4, 25_000_000)
+    nb, mx = api.rar_bucket_count(b)
+    assert nb == len(ref) == 118 and mx == 6_250_000
+    pos = 0
+    for k, segs in enumerate(ref):
+        so, el, ns = api.rar_bucket_info(b, k)
+        assert so == pos and el == sum(s[3] for s in segs) and ns == len(segs)
+        for j, seg in enumerate(segs):
+            assert api.rar_bucket_segment(b, k, j) == tuple(seg)
+        pos += el
+    assert api.rar_bucket_info(b, 117)[1] == 4_121_264
+
+
+@pytest.mark.parametrize("numels,bb,dt", [([5, 0, 7, 100, 1], 8, 0), ([3] * 10, 4, 1), ([], 16, 0),
+                                          ([1000], 4000, 0), ([1000], 4004, 0)])
+def test_bucket_layout_small_cases(numels, bb, dt):
+    b = api.rar_bucket_plan(numels, dt, bb)
+    ref = oracle.bucket_layout(numels, 4 if dt == 0 else 2, bb)
+    assert api.rar_bucket_count(b)[0] == len(ref)
+    for k, segs in enumerate(ref):
+        assert [api.rar_bucket_segment(b, k, j) for j in range(len(segs))] == [tuple(s) for s in segs]
+
+
+def test_bucket_plan_rejects_bad_arguments():
+    for args in (([1, -1], 0, 16), ([1], 0, 3), ([1], 5, 16), ([1], 1, 1)):
+        with pytest.raises(api.RarError):
+            api.rar_bucket_plan(*args)

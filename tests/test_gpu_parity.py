@@ -1,0 +1,387 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Binary32 results must be bit-identical to the oracle (same ring order, same
+IEEE operations).  bf16 results must be bit-identical to the oracle's bf16
+variant and within 1e-2 of a float64 mean (max |error| / max |mean|).  Small
+and ragged cases run the oracle in full; the full-size workloads compare
+sampled elements (every chunk boundary +-9 and 10^6 random ones) through the
+oracle's literal ring restricted to those elements, plus whole-array
+properties (all ranks identical).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_all_reduce_amd import api, synth
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _host_f32(N, P, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return [(rng.standard_normal(P) * scale).astype(np.float32) for _ in range(N)]
+
+
+def _host_bf16(N, P, seed, scale=1e-3):
+    # Student-t(3) draws rounded to bf16 by torch (input generation only)
+    return [synth.student_t3_bf16(P, seed * 1000 + r, scale, "cpu").view(torch.int16).numpy().view(np.uint16)
+            for r in range(N)]
+
+
+def _to_dev(arrs):
+    return [torch.from_numpy(a.copy()).to(DEV) for a in arrs]
+
+
+def _bf16_dev(arrs):
+    return [torch.from_numpy(a.view(np.int16).copy()).to(DEV).view(torch.bfloat16) for a in arrs]
+
+
+def _bits16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _first_diff(a, b):
+    d = np.flatnonzero(a != b)
+    return int(d[0]) if d.size else None
+
+
+def _assert_bits(got, ref, what):
+    if got.tobytes() != ref.tobytes():
+        nan = np.isnan(ref) if ref.dtype == np.float32 else None
+        if nan is not None and np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan], ref[~nan]):
+            return  # NaN payloads are not part of the contract
+        i = _first_diff(got, ref)
+        raise AssertionError(f"{what}: first difference at {i}: got {got[i]!r} expected {ref[i]!r}")
+
+
+F32_CASES = [(1, 1), (1, 1001), (2, 1), (2, 2), (2, 9), (3, 5), (4, 3), (8, 7), (5, 4097), (7, 16),
+             (4, 1_000_003), (13, 100_003), (40, 12_345), (64, 1), (64, 1000), (64, 65_539)]
+
+
+@pytest.mark.parametrize("N,P", F32_CASES)
+@pytest.mark.parametrize("mode", [api.BALANCED, api.CEIL, api.ALIGN16])
+@pytest.mark.parametrize("algo", [api.FUSED, api.RING, api.NAIVE])
+def test_f32_mean_and_sgd_bit_exact(N, P, mode, algo):
+    g = _host_f32(N, P, 1000 + N * 7 + P % 1000)
+    w0 = np.random.default_rng(5).uniform(-0.05, 0.05, P).astype(np.float32)
+    for sgd in (False, True):
+        d = _to_dev(g)
+        wd = torch.from_numpy(w0.copy()).to(DEV)
+        plan = api.rar_plan(N, P, api.F32, mode)
+        api.rar_plan_set_algo(plan, algo)
+        if sgd:
+            api.rar_allreduce_sgd(plan, d, wd, 0.1, P)
+        else:
+            api.rar_allreduce_mean(plan, d, P)
+        torch.cuda.synchronize()
+        ref = [x.copy() for x in g]
+        wr = w0.copy()
+        if algo == api.NAIVE:
+            oracle.naive_reduce_f32(ref, wr if sgd else None, 0.1)
+        else:
+            oracle.ring_allreduce_f32(ref, oracle.partition(N, P, mode, 4), wr if sgd else None, 0.1)
+        for n in range(N):
+            _assert_bits(d[n].cpu().numpy(), ref[n], f"rank {n} sgd={sgd}")
+        if sgd:
+            _assert_bits(wd.cpu().numpy(), wr, "weights")
+
+
+BF16_CASES = [(1, 9), (2, 17), (3, 1001), (8, 8), (8, 1_000_003), (40, 100_007), (64, 777), (5, 3)]
+
+
+@pytest.mark.parametrize("N,P", BF16_CASES)
+@pytest.mark.parametrize("mode", [api.BALANCED, api.CEIL, api.ALIGN16])
+@pytest.mark.parametrize("algo", [api.FUSED, api.RING])
+def test_bf16_bit_exact_and_within_tolerance(N, P, mode, algo):
+    g = _host_bf16(N, P, 77 + N + P % 97)
+    w0 = np.random.default_rng(6).uniform(-0.02, 0.02, P).astype(np.float32)
+    for sgd in (False, True):
+        d = _bf16_dev(g)
+        wd = torch.from_numpy(w0.copy()).to(DEV)
+        plan = api.rar_plan(N, P, api.BF16, mode)
+        api.rar_plan_set_algo(plan, algo)
+        if sgd:
+            api.rar_allreduce_sgd(plan, d, wd, 1e-4, P)
+        else:
+            api.rar_allreduce_mean(plan, d, P)
+        torch.cuda.synchronize()
+        ref = [x.copy() for x in g]
+        wr = w0.copy()
+        oracle.ring_allreduce_bf16(ref, oracle.partition(N, P, mode, 2), wr if sgd else None, 1e-4)
+        for n in range(N):
+            got = _bits16(d[n])
+            assert got.tobytes() == ref[n].tobytes(), f"rank {n}: first diff {_first_diff(got, ref[n])}"
+        if sgd:
+            _assert_bits(wd.cpu().numpy(), wr, "weights")
+        exact = np.stack([oracle.bf16_to_f32(x) for x in g]).astype(np.float64).sum(0) / N
+        y = oracle.bf16_to_f32(_bits16(d[0])).astype(np.float64)
+        if np.max(np.abs(exact)) > 0:
+            assert np.max(np.abs(y - exact)) / np.max(np.abs(exact)) <= 1e-2
+
+
+def test_resnet18_sized_sgd_all_algorithms():
+    wl = synth.WORKLOADS[2]
+    N, P = wl.N, wl.P
+    g = [t.cpu().numpy() for t in synth.rank_gradients(wl, "cpu")]
+    w0 = synth.weights(wl, "cpu").numpy()
+    ref = [x.copy() for x in g]
+    wr = w0.copy()
+    oracle.ring_allreduce_f32(ref, oracle.partition(N, P), wr, wl.lr)
+    for algo in (api.FUSED, api.RING):
+        d = _to_dev(g)
+        wd = torch.from_numpy(w0.copy()).to(DEV)
+        plan = api.rar_plan(N, P)
+        api.rar_plan_set_algo(plan, algo)
+        api.rar_allreduce_sgd(plan, d, wd, wl.lr, P)
+        torch.cuda.synchronize()
+        for n in (0, 3, N - 1):
+            _assert_bits(d[n].cpu().numpy(), ref[n], f"algo {algo} rank {n}")
+        for n in range(1, N):
+            assert torch.equal(d[n], d[0])
+        _assert_bits(wd.cpu().numpy(), wr, f"algo {algo} weights")
+
+
+@pytest.mark.parametrize("N,P", [(1, 100), (2, 9), (4, 1_000_003), (10, 123_457), (40, 40_001), (64, 64)])
+def test_reduce_scatter_owner_sgd_allgather(N, P):
+    g = _host_f32(N, P, 31 + N)
+    w0 = np.random.default_rng(2).uniform(-0.05, 0.05, P).astype(np.float32)
+    d = _to_dev(g)
+    wreps = [torch.from_numpy(w0.copy()).to(DEV) for _ in range(N)]
+    plan = api.rar_plan(N, P)
+    api.rar_reduce_scatter_sgd_allgather(plan, d, wreps, 0.05, P)
+    torch.cuda.synchronize()
+    ref = [x.copy() for x in g]
+    wr = w0.copy()
+    off = oracle.partition(N, P)
+    oracle.ring_allreduce_f32(ref, off, wr, 0.05)
+    for n in range(N):
+        _assert_bits(wreps[n].cpu().numpy(), wr, f"replica {n}")
+    for c in range(N):
+        o = oracle.owner(c, N)
+        _assert_bits(d[o].cpu().numpy()[off[c]:off[c + 1]], ref[o][off[c]:off[c + 1]], f"owner of chunk {c}")
+
+
+@pytest.mark.parametrize("grid", [1, 2, 7, 64, 1000, 0])
+def test_results_do_not_depend_on_launch_shape(grid):
+    N, P = 4, 1_000_003
+    g = _host_f32(N, P, 4)
+    ref = [x.copy() for x in g]
+    oracle.ring_allreduce_f32(ref, oracle.partition(N, P))
+    for algo in (api.FUSED, api.RING):
+        for rep in range(3):
+            d = _to_dev(g)
+            plan = api.rar_plan(N, P)
+            api.rar_plan_set_algo(plan, algo)
+            api.rar_plan_set_grid(plan, grid)
+            api.rar_allreduce_mean(plan, d, P)
+            torch.cuda.synchronize()
+            for n in range(N):
+                _assert_bits(d[n].cpu().numpy(), ref[n], f"grid {grid} algo {algo} rep {rep} rank {n}")
+
+
+def test_special_values():
+    N, P = 6, 40_009
+    g = _host_f32(N, P, 9)
+    off = oracle.partition(N, P)
+    for c in range(1, N):
+        g[c % N][off[c]] = np.inf
+        g[(c + 1) % N][off[c] - 1] = np.nan
+        g[c % N][off[c] + 1] = np.float32(3e-45)  # subnormal
+        g[(c + 2) % N][off[c] + 2] = -np.inf
+        g[(c + 3) % N][off[c] + 2] = np.inf  # inf - inf
+    for algo in (api.FUSED, api.RING):
+        d = _to_dev(g)
+        plan = api.rar_plan(N, P)
+        api.rar_plan_set_algo(plan, algo)
+        api.rar_allreduce_mean(plan, d, P)
+        torch.cuda.synchronize()
+        ref = [x.copy() for x in g]
+        oracle.ring_allreduce_f32(ref, off)
+        for n in range(N):
+            _assert_bits(d[n].cpu().numpy(), ref[n], f"algo {algo} rank {n}")
+
+
+def test_runs_on_the_given_stream():
+    N, P = 8, 2_000_000
+    g = _host_f32(N, P, 12)
+    ref = [x.copy() for x in g]
+    oracle.ring_allreduce_f32(ref, oracle.partition(N, P))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        d = _to_dev(g)
+        plan = api.rar_plan(N, P)
+        api.rar_allreduce_mean(plan, d, P, stream=s)
+    s.synchronize()
+    for n in range(N):
+        _assert_bits(d[n].cpu().numpy(), ref[n], f"rank {n}")
+
+
+# ---------------------------------------------------------------------------
+# Buckets
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", [api.F32, api.BF16])
+def test_bucket_pack_unpack_roundtrip_unaligned(dt):
+    tdt = torch.float32 if dt == api.F32 else torch.bfloat16
+    es = 4 if dt == api.F32 else 2
+    numels = [5, 1, 1000, 3, 77, 4096, 2]
+    N = 3
+    arenas = [torch.randn(sum(numels) + 7, device=DEV).to(tdt) for _ in range(N)]
+    tensors, pos = [], 1  # odd start: every tensor misaligned
+    for n in range(N):
+        ts, p = [], pos
+        for k in numels:
+            ts.append(arenas[n][p:p + k])
+            p += k
+        tensors.append(ts)
+    b = api.rar_bucket_plan(numels, dt, 96 * es)
+    nb, mx = api.rar_bucket_count(b)
+    bufs = [torch.zeros(mx, dtype=tdt, device=DEV) for _ in range(N)]
+    backup = [a.clone() for a in arenas]
+    layout = oracle.bucket_layout(numels, es, 96 * es)
+    for k in range(nb):
+        api.rar_bucket_pack(b, k, tensors, bufs)
+        torch.cuda.synchronize()
+        for n in range(N):
+            for (t, toff, boff, ln) in layout[k]:
+                assert torch.equal(bufs[n][boff:boff + ln], tensors[n][t][toff:toff + ln])
+        for n in range(N):
+            for (t, toff, boff, ln) in layout[k]:
+                tensors[n][t][toff:toff + ln].zero_()
+        api.rar_bucket_unpack(b, k, bufs, tensors)
+    torch.cuda.synchronize()
+    for n in range(N):
+        assert torch.equal(arenas[n], backup[n])
+
+
+def test_bucketed_small_transformer_bit_exact():
+    N = 4
+    specs = synth.transformer_tensors(2, d=64, h=256, V=1000)
+    numels = [s.numel for s in specs]
+    bucket_bytes = 4 * 40_000
+    host = [[np.random.default_rng(100 * n + t).standard_normal(s.numel).astype(np.float32) * 1e-3
+             for t, s in enumerate(specs)] for n in range(N)]
+    for algo in (api.FUSED, api.RING):
+        tensors = [[torch.from_numpy(x.copy()).to(DEV) for x in rank] for rank in host]
+        b = api.rar_bucket_plan(numels, api.F32, bucket_bytes)
+        _, mx = api.rar_bucket_count(b)
+        bufs = [torch.empty(mx, device=DEV) for _ in range(N)]
+        api.rar_bucket_allreduce_mean(b, tensors, bufs, api.BALANCED, algo)
+        torch.cuda.synchronize()
+        ref = [[x.copy() for x in rank] for rank in host]
+        oracle.bucketed_ring_f32(ref, bucket_bytes)
+        for n in range(N):
+            for t in range(len(specs)):
+                _assert_bits(tensors[n][t].cpu().numpy(), ref[n][t], f"algo {algo} rank {n} tensor {t}")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled
+# ---------------------------------------------------------------------------
+
+def _samples(off, P, k, seed):
+    rng = np.random.default_rng(seed)
+    edges = np.array([o + dlt for o in off for dlt in range(-9, 10)], dtype=np.int64)
+    idx = np.unique(np.concatenate([edges, rng.integers(0, P, k)]))
+    return idx[(idx >= 0) & (idx < P)]
+
+
+def _gather(ts, idx_d):
+    return [t[idx_d].cpu().numpy() for t in ts]
+
+
+@pytest.mark.parametrize("algo", [api.FUSED, api.RING])
+def test_full_size_300m_sgd_sampled(algo):
+    wl = synth.WORKLOADS[3]
+    N, P = wl.N, wl.P
+    off = oracle.partition(N, P)
+    idx = _samples(off, P, 1_000_000, 3)
+    idx_d = torch.from_numpy(idx).to(DEV)
+    g = synth.rank_gradients(wl, DEV)
+    w = synth.weights(wl, DEV)
+    pre = _gather(g, idx_d)
+    wpre = w[idx_d].cpu().numpy()
+    plan = api.rar_plan(N, P)
+    api.rar_plan_set_algo(plan, algo)
+    api.rar_allreduce_sgd(plan, g, w, wl.lr, P)
+    torch.cuda.synchronize()
+    for n in range(1, N):
+        assert torch.equal(g[n], g[0]), f"rank {n} differs from rank 0"
+    oracle.ring_allreduce_f32(pre, oracle.compact_layout(off, idx), wpre, wl.lr)
+    post = _gather(g, idx_d)
+    for n in (0, N - 1):
+        _assert_bits(post[n], pre[n], f"rank {n} (sampled)")
+    _assert_bits(w[idx_d].cpu().numpy(), wpre, "weights (sampled)")
+
+
+@pytest.mark.parametrize("algo", [api.FUSED, api.RING])
+def test_full_size_40_rank_bf16_sampled(algo):
+    wl = synth.WORKLOADS[5]
+    N, P = wl.N, wl.P
+    off = oracle.partition(N, P, 0, 2)
+    idx = _samples(off, P, 500_000, 5)
+    idx_d = torch.from_numpy(idx).to(DEV)
+    g = synth.rank_gradients(wl, DEV)
+    w = synth.weights(wl, DEV)
+    pre = [_bits16(t[idx_d]) for t in g]
+    wpre = w[idx_d].cpu().numpy()
+    plan = api.rar_plan(N, P, api.BF16)
+    api.rar_plan_set_algo(plan, algo)
+    api.rar_allreduce_sgd(plan, g, w, wl.lr, P)
+    torch.cuda.synchronize()
+    for n in range(1, N):
+        assert torch.equal(g[n].view(torch.int16), g[0].view(torch.int16)), f"rank {n} differs"
+    exact = np.stack([oracle.bf16_to_f32(x) for x in pre]).astype(np.float64).sum(0) / N
+    oracle.ring_allreduce_bf16(pre, oracle.compact_layout(off, idx), wpre, wl.lr)
+    post = _bits16(g[0][idx_d])
+    assert post.tobytes() == pre[0].tobytes(), f"first diff {_first_diff(post, pre[0])}"
+    _assert_bits(w[idx_d].cpu().numpy(), wpre, "weights (sampled)")
+    y = oracle.bf16_to_f32(post).astype(np.float64)
+    assert np.max(np.abs(y - exact)) / np.max(np.abs(exact)) <= 1e-2
+
+
+@pytest.mark.parametrize("path", ["pack", "arena"])
+def test_full_size_transformer_buckets_sampled(path):
+    wl = synth.WORKLOADS[4]
+    N = wl.N
+    specs, ranks = synth.transformer_rank_tensors(wl, DEV)
+    numels = [s.numel for s in specs]
+    total = sum(numels)
+    arenas = [flat for (flat, _) in ranks]
+    tensors = [ts for (_, ts) in ranks]
+    b = api.rar_bucket_plan(numels, api.F32, wl.bucket_bytes)
+    nb, mx = api.rar_bucket_count(b)
+    assert nb == 118
+    rng = np.random.default_rng(44)
+    per_bucket = []
+    for k in range(nb):
+        so, el, _ = api.rar_bucket_info(b, k)
+        off = oracle.partition(N, el)
+        idx = _samples(off, el, 2000, int(rng.integers(1 << 30)))
+        per_bucket.append((so, el, off, idx))
+    all_idx = np.concatenate([so + idx for (so, _, _, idx) in per_bucket])
+    idx_d = torch.from_numpy(all_idx).to(DEV)
+    pre = _gather(arenas, idx_d)
+    if path == "pack":
+        bufs = [torch.empty(mx, device=DEV) for _ in range(N)]
+        api.rar_bucket_allreduce_mean(b, tensors, bufs)
+    else:
+        plans = {}
+        for (so, el, _, _) in per_bucket:
+            if el not in plans:
+                plans[el] = api.rar_plan(N, el)
+            api.rar_allreduce_mean(plans[el], [a[so:so + el] for a in arenas], el)
+    torch.cuda.synchronize()
+    for n in range(1, N):
+        assert torch.equal(arenas[n], arenas[0])
+    post = _gather(arenas, idx_d)
+    pos = 0
+    for (so, el, off, idx) in per_bucket:
+        sl = slice(pos, pos + len(idx))
+        sub = [np.ascontiguousarray(p[sl]) for p in pre]
+        oracle.ring_allreduce_f32(sub, oracle.compact_layout(off, idx))
+        _assert_bits(post[0][sl], sub[0], f"bucket at {so}")
+        pos += len(idx)
+    assert pos == len(all_idx) and total == 735_371_264
