@@ -244,6 +244,9 @@ def secondary_rows(dev, stream, reps=5):
     cal = CopyCalibration(dev)
     add("copy_1.2GB_rar_copy_kernel", cal.bytes, lambda: cal.run_once(stream))
     add("copy_1.2GB_torch_copy_", cal.bytes, lambda: cal.dst.copy_(cal.src))
+    # one-stream read-only and write-only references (torch reductions / fills)
+    add("read_1.2GB_torch_sum", cal.bytes // 2, lambda: cal.src.sum())
+    add("write_1.2GB_torch_fill_", cal.bytes // 2, lambda: cal.dst.fill_(0.5))
     del cal
     torch.cuda.empty_cache()
 
@@ -320,7 +323,7 @@ def secondary_rows(dev, stream, reps=5):
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl, dev, sample_P=60_000_000, min_s=10.0, max_s=30.0):
+def cpu_baseline(wl, dev, sample_P=100_000_000, min_s=10.0, max_s=30.0):
     import numpy as np
     import oracle
     from ring_all_reduce_amd import synth
@@ -330,7 +333,7 @@ def cpu_baseline(wl, dev, sample_P=60_000_000, min_s=10.0, max_s=30.0):
     w = synth.weights(wl, dev, P=P).cpu().numpy()
     off = oracle.partition(N, P)
     runs, t_sum = 0, 0.0
-    while t_sum < min_s and runs < 20:
+    while t_sum < min_s and runs < 200:
         t0 = time.perf_counter()
         oracle.ring_allreduce_f32(g, off, w, wl.lr or 0.0)
         t_sum += time.perf_counter() - t0
@@ -340,8 +343,9 @@ def cpu_baseline(wl, dev, sample_P=60_000_000, min_s=10.0, max_s=30.0):
     per = t_sum / runs
     nb = alg_bytes(N, P, 4, wl.lr is not None)
     return {"value": round(nb / per / 1e9, 3), "unit": "GB/s", "cores": oracle.get_threads(), "kind": "oracle",
-            "sample": f"{N} ranks x {P} fp32 elements (first {P} of the workload's shape, same seeds and "
-                      f"distribution), literal ring with SGD, {runs} runs, {per:.3f} s per run",
+            "sample": f"{N} ranks x {P} fp32 elements per rank drawn with the workload's seeds and "
+                      f"distribution (the full workload has {wl.P}), literal ring with SGD, {runs} runs, "
+                      f"{per:.3f} s per run, {t_sum:.1f} s in all",
             "cpu": _cpu_model()}
 
 

@@ -15,7 +15,8 @@ Workloads follow the shapes on the pages (short names as elsewhere):
     per-layer Q,K,V,O, two FFN matrices, their biases and two LayerNorms
     ([GPipe explainer] §1, the parameter-count fit P(L)).
   * A 40-rank bf16 case with heavy-tailed (Student-t, 3 degrees of freedom)
-    values; the pages fix no bf16 workload, this one is named by the task.
+    values.  The pages fix no bf16 workload; this one exercises bf16
+    storage with binary32 accumulation at a large rank count.
 """
 from __future__ import annotations
 
