@@ -178,7 +178,8 @@ def main():
         "params_per_s": round(P / (ms_per_step * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"rar_fused_{'f32' if es == 4 else 'bf16'}" if args.algo == "fused" else "ring steps",
+            "kernel": (f"rar_fused_{'f32' if es == 4 else 'bf16'}"
+                       f"{'_grp' if N in (2, 4, 8, 10, 16, 40) else ''}") if args.algo == "fused" else "ring steps",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

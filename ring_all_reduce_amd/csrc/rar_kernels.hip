@@ -354,6 +354,270 @@ __global__ __launch_bounds__(kThreads) void rar_fused_bf16(FusedParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Fused single pass with the work of one tile split over G lane groups.
+// ---------------------------------------------------------------------------
+//
+// Same arithmetic as rar_fused_f32 / rar_fused_bf16, same bits.  A workgroup
+// is G groups of kThreads lanes working on one tile of kThreads vectors.  The
+// fold positions 0..N-1 of chunk c (rank (c+k) mod N at position k) are cut
+// into G consecutive runs, one per group: every group loads only its run's
+// vectors and, once the mean is known, stores only to its run's ranks; the
+// last group also reads and writes w.  The partial sum passes from group to
+// group through one LDS slot in fold order, so the additions happen in
+// exactly the ring order; the last group divides by N and publishes the mean
+// through a second slot.  G barriers per tile; LDS 8 KiB (binary32) or
+// 16 KiB (bf16) whatever N is.
+//
+// Why: with one lane doing all N loads and N stores a lane has 2N+2 memory
+// operations per tile.  Spreading them over G groups gives each wave fewer
+// back-to-back stores, and HBM drains several concurrent write streams
+// faster that way (measured on MI355X, 10 ranks x 300M with SGD: ~5.45 TB/s
+// with one group, ~5.75 TB/s with two to four).
+
+// Scalar path for the at most VEC-1 elements before the first and after the
+// last aligned 16-byte group of a chunk (block 0 of the chunk, lanes < 2*VEC).
+template <typename T, int VEC, int NT, bool SGD>
+__device__ __forceinline__ void fused_head_tail(const FusedParams &p, int c, int64_t e0, int64_t e1,
+                                                int64_t a0, int64_t a1)
+{
+    if (blockIdx.x != 0 || threadIdx.x >= 2 * VEC)
+        return;
+    const int t = threadIdx.x;
+    int64_t e = -1;
+    if (t < a0 - e0)
+        e = e0 + t;
+    else if (t >= VEC && t < VEC + (e1 - a1))
+        e = a1 + (t - VEC);
+    if (e < 0)
+        return;
+    auto val = [&](int r) -> float {
+        if constexpr (sizeof(T) == 4)
+            return static_cast<const float *>(p.bufs.p[r])[e];
+        else
+            return bf16_one(static_cast<const uint16_t *>(p.bufs.p[r])[e]);
+    };
+    float acc = val(c);
+    int r = c;
+    for (int k = 1; k < NT; ++k) {
+        r = next_rank(r, NT);
+        acc = acc + val(r);
+    }
+    const float m = acc / (float)NT;
+    for (int n = 0; n < NT; ++n) {
+        if constexpr (sizeof(T) == 4)
+            static_cast<float *>(p.bufs.p[n])[e] = m;
+        else
+            static_cast<uint16_t *>(p.bufs.p[n])[e] = (uint16_t)bf16_rne(m);
+    }
+    if (SGD) {
+        const float step = p.lr * m;
+        p.w[e] = p.w[e] - step;
+    }
+}
+
+template <int NT, int G, bool SGD>
+__global__ __launch_bounds__(kThreads *G) void rar_fused_f32_grp(FusedParams p)
+{
+    static_assert(NT > 0 && G >= 1, "compile-time rank count");
+    constexpr int PER = (NT + G - 1) / G;
+    const int c = blockIdx.y;
+    const int g = threadIdx.x / kThreads;
+    const int lane = threadIdx.x % kThreads;
+    const int k0 = g * PER;
+    const int cnt = k0 >= NT ? 0 : (NT - k0 < PER ? NT - k0 : PER);
+    __shared__ f32x4 chain[G > 1 ? kThreads : 1];
+    __shared__ f32x4 mean[G > 1 ? kThreads : 1];
+
+    const int64_t e0 = p.ct.off[c], e1 = p.ct.off[c + 1];
+    if (e1 <= e0)
+        return;
+    int64_t a0 = (e0 + 3) / 4 * 4, a1 = e1 / 4 * 4;
+    if (a0 > a1) {
+        a0 = e1;
+        a1 = e1;
+    }
+    fused_head_tail<float, 4, NT, SGD>(p, c, e0, e1, a0, a1);
+    const int64_t nvec = (a1 - a0) / 4;
+    const int64_t ntiles = (nvec + kThreads - 1) / kThreads;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t v = t * kThreads + lane;
+        const bool ok = v < nvec;
+        f32x4 x[PER];
+        f32x4 wv = {0.f, 0.f, 0.f, 0.f};
+        if (ok) {
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                if (j < cnt) {
+                    int r = c + k0 + j;
+                    r = r >= NT ? r - NT : r;
+                    x[j] = ld(vec_at<const f32x4, const float>(p.bufs.p[r], a0) + v);
+                }
+            }
+            if (SGD && g == G - 1)
+                wv = ld(vec_at<const f32x4, const float>(p.w, a0) + v);
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (g == 0 && ok) {
+            acc = x[0];
+#pragma unroll
+            for (int j = 1; j < PER; ++j)
+                if (j < cnt)
+                    acc = acc + x[j];
+        }
+        f32x4 m;
+        if constexpr (G > 1) {
+#pragma unroll
+            for (int h = 1; h < G; ++h) {
+                if (g == h - 1)
+                    chain[lane] = acc;
+                __syncthreads();
+                if (g == h && ok) {
+                    acc = chain[lane];
+#pragma unroll
+                    for (int j = 0; j < PER; ++j)
+                        if (j < cnt)
+                            acc = acc + x[j];
+                }
+            }
+            if (g == G - 1)
+                mean[lane] = acc / (float)NT;
+            __syncthreads();
+            m = mean[lane];
+        } else {
+            m = acc / (float)NT;
+        }
+        if (ok) {
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                if (j < cnt) {
+                    int r = c + k0 + j;
+                    r = r >= NT ? r - NT : r;
+                    st(vec_at<f32x4, float>(p.bufs.p[r], a0) + v, m);
+                }
+            }
+            if (SGD && g == G - 1) {
+                const f32x4 step = p.lr * m;
+                wv = wv - step;
+                st(vec_at<f32x4, float>(p.w, a0) + v, wv);
+            }
+        }
+    }
+}
+
+template <int NT, int G, bool SGD>
+__global__ __launch_bounds__(kThreads *G) void rar_fused_bf16_grp(FusedParams p)
+{
+    static_assert(NT > 0 && G >= 1, "compile-time rank count");
+    constexpr int PER = (NT + G - 1) / G;
+    const int c = blockIdx.y;
+    const int g = threadIdx.x / kThreads;
+    const int lane = threadIdx.x % kThreads;
+    const int k0 = g * PER;
+    const int cnt = k0 >= NT ? 0 : (NT - k0 < PER ? NT - k0 : PER);
+    __shared__ f32x4 chain[G > 1 ? 2 * kThreads : 1];
+    __shared__ f32x4 mean[G > 1 ? 2 * kThreads : 1];
+
+    const int64_t e0 = p.ct.off[c], e1 = p.ct.off[c + 1];
+    if (e1 <= e0)
+        return;
+    int64_t a0 = (e0 + 7) / 8 * 8, a1 = e1 / 8 * 8;
+    if (a0 > a1) {
+        a0 = e1;
+        a1 = e1;
+    }
+    fused_head_tail<uint16_t, 8, NT, SGD>(p, c, e0, e1, a0, a1);
+    const int64_t nvec = (a1 - a0) / 8;
+    const int64_t ntiles = (nvec + kThreads - 1) / kThreads;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t v = t * kThreads + lane;
+        const bool ok = v < nvec;
+        u32x4 x[PER];
+        f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
+        if (ok) {
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                if (j < cnt) {
+                    int r = c + k0 + j;
+                    r = r >= NT ? r - NT : r;
+                    x[j] = ld(vec_at<const u32x4, const uint16_t>(p.bufs.p[r], a0) + v);
+                }
+            }
+            if (SGD && g == G - 1) {
+                const f32x4 *wp = vec_at<const f32x4, const float>(p.w, a0);
+                w0 = ld(wp + 2 * v);
+                w1 = ld(wp + 2 * v + 1);
+            }
+        }
+        f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+        if (g == 0 && ok) {
+            widen8(x[0], lo, hi);
+#pragma unroll
+            for (int j = 1; j < PER; ++j) {
+                if (j < cnt) {
+                    f32x4 a, b;
+                    widen8(x[j], a, b);
+                    lo = lo + a;
+                    hi = hi + b;
+                }
+            }
+        }
+        f32x4 mlo, mhi;
+        if constexpr (G > 1) {
+#pragma unroll
+            for (int h = 1; h < G; ++h) {
+                if (g == h - 1) {
+                    chain[2 * lane] = lo;
+                    chain[2 * lane + 1] = hi;
+                }
+                __syncthreads();
+                if (g == h && ok) {
+                    lo = chain[2 * lane];
+                    hi = chain[2 * lane + 1];
+#pragma unroll
+                    for (int j = 0; j < PER; ++j) {
+                        if (j < cnt) {
+                            f32x4 a, b;
+                            widen8(x[j], a, b);
+                            lo = lo + a;
+                            hi = hi + b;
+                        }
+                    }
+                }
+            }
+            if (g == G - 1) {
+                mean[2 * lane] = lo / (float)NT;
+                mean[2 * lane + 1] = hi / (float)NT;
+            }
+            __syncthreads();
+            mlo = mean[2 * lane];
+            mhi = mean[2 * lane + 1];
+        } else {
+            mlo = lo / (float)NT;
+            mhi = hi / (float)NT;
+        }
+        if (ok) {
+            const u32x4 out = narrow8(mlo, mhi);
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                if (j < cnt) {
+                    int r = c + k0 + j;
+                    r = r >= NT ? r - NT : r;
+                    st(vec_at<u32x4, uint16_t>(p.bufs.p[r], a0) + v, out);
+                }
+            }
+            if (SGD && g == G - 1) {
+                f32x4 *wp = vec_at<f32x4, float>(p.w, a0);
+                const f32x4 s0 = p.lr * mlo, s1 = p.lr * mhi;
+                w0 = w0 - s0;
+                w1 = w1 - s1;
+                st(wp + 2 * v, w0);
+                st(wp + 2 * v + 1, w1);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // One scatter-reduce step, binary32, all N transfers of the step at once.
 // ---------------------------------------------------------------------------
 //
@@ -641,53 +905,71 @@ int blocks_x(int max_blocks, int jobs, int64_t max_vecs, int vpt)
     return (int)bx;
 }
 
-template <int NT>
-hipError_t fused_f32_n(const FusedParams &p, bool sgd, dim3 g, hipStream_t st)
-{
-    constexpr int VPT = (NT > 0 && NT <= 16) ? 2 : 1;
-    if (sgd)
-        hipLaunchKernelGGL((rar_fused_f32<NT, VPT, true>), g, dim3(kThreads), 0, st, p);
-    else
-        hipLaunchKernelGGL((rar_fused_f32<NT, VPT, false>), g, dim3(kThreads), 0, st, p);
-    return hipGetLastError();
-}
+// Lane groups per workgroup of the grouped fused kernels, by rank count and
+// element type, from a sweep on MI355X over 1-4 groups (fused pass with and
+// without SGD at 4, 8, 10, 16 and 40 ranks): binary32 gains from splitting a
+// tile over up to four groups; bf16, with twice the elements and the widening
+// per lane and a 32-byte partial sum to pass, gains from two groups at
+// 4-16 ranks and loses from any split at 40.
+constexpr int groups_f32(int N) { return N <= 3 ? 1 : N <= 4 ? 2 : N <= 12 ? 4 : N <= 16 ? 3 : 4; }
+constexpr int groups_bf16(int N) { return N <= 3 ? 1 : N <= 16 ? 2 : 1; }
 
 template <int NT>
-hipError_t fused_bf16_n(const FusedParams &p, bool sgd, dim3 g, hipStream_t st)
+hipError_t fused_grouped(rar_dtype dt, const FusedParams &p, int max_blocks, int64_t max_chunk,
+                         hipStream_t st)
 {
-    if (sgd)
-        hipLaunchKernelGGL((rar_fused_bf16<NT, true>), g, dim3(kThreads), 0, st, p);
-    else
-        hipLaunchKernelGGL((rar_fused_bf16<NT, false>), g, dim3(kThreads), 0, st, p);
+    const bool sgd = p.w != nullptr;
+    if (dt == RAR_F32) {
+        constexpr int G = groups_f32(NT);
+        const dim3 g(blocks_x(max_blocks, NT, max_chunk / 4 + 1, 1), NT), b(kThreads * G);
+        if (sgd)
+            hipLaunchKernelGGL((rar_fused_f32_grp<NT, G, true>), g, b, 0, st, p);
+        else
+            hipLaunchKernelGGL((rar_fused_f32_grp<NT, G, false>), g, b, 0, st, p);
+    } else {
+        constexpr int G = groups_bf16(NT);
+        const dim3 g(blocks_x(max_blocks, NT, max_chunk / 8 + 1, 1), NT), b(kThreads * G);
+        if (sgd)
+            hipLaunchKernelGGL((rar_fused_bf16_grp<NT, G, true>), g, b, 0, st, p);
+        else
+            hipLaunchKernelGGL((rar_fused_bf16_grp<NT, G, false>), g, b, 0, st, p);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Rank counts with a compile-time kernel (the workloads' 4, 8, 10 and 40, and
+// the powers of two up to 16) take the grouped kernels; any other N takes the
+// runtime-N single-group kernels.
 hipError_t launch_fused(rar_dtype dt, const FusedParams &p, int max_blocks, int64_t max_chunk,
                         hipStream_t st)
 {
-    const bool sgd = p.w != nullptr;
-    if (dt == RAR_F32) {
-        const int vpt = (p.N <= 16) ? 2 : 1;
-        const dim3 g(blocks_x(max_blocks, p.N, max_chunk / 4 + 1, vpt), p.N);
-        switch (p.N) {
-        case 4: return fused_f32_n<4>(p, sgd, g, st);
-        case 8: return fused_f32_n<8>(p, sgd, g, st);
-        case 10: return fused_f32_n<10>(p, sgd, g, st);
-        case 40: return fused_f32_n<40>(p, sgd, g, st);
-        default: {
-            const dim3 g1(blocks_x(max_blocks, p.N, max_chunk / 4 + 1, 1), p.N);
-            return fused_f32_n<0>(p, sgd, g1, st);
-        }
-        }
-    }
-    const dim3 g(blocks_x(max_blocks, p.N, max_chunk / 8 + 1, 1), p.N);
     switch (p.N) {
-    case 8: return fused_bf16_n<8>(p, sgd, g, st);
-    case 40: return fused_bf16_n<40>(p, sgd, g, st);
-    default: return fused_bf16_n<0>(p, sgd, g, st);
+    case 2: return fused_grouped<2>(dt, p, max_blocks, max_chunk, st);
+    case 4: return fused_grouped<4>(dt, p, max_blocks, max_chunk, st);
+    case 8: return fused_grouped<8>(dt, p, max_blocks, max_chunk, st);
+    case 10: return fused_grouped<10>(dt, p, max_blocks, max_chunk, st);
+    case 16: return fused_grouped<16>(dt, p, max_blocks, max_chunk, st);
+    case 40: return fused_grouped<40>(dt, p, max_blocks, max_chunk, st);
+    default: break;
     }
+    const bool sgd = p.w != nullptr;
+    const dim3 b(kThreads);
+    if (dt == RAR_F32) {
+        const dim3 g(blocks_x(max_blocks, p.N, max_chunk / 4 + 1, 1), p.N);
+        if (sgd)
+            hipLaunchKernelGGL((rar_fused_f32<0, 1, true>), g, b, 0, st, p);
+        else
+            hipLaunchKernelGGL((rar_fused_f32<0, 1, false>), g, b, 0, st, p);
+    } else {
+        const dim3 g(blocks_x(max_blocks, p.N, max_chunk / 8 + 1, 1), p.N);
+        if (sgd)
+            hipLaunchKernelGGL((rar_fused_bf16<0, true>), g, b, 0, st, p);
+        else
+            hipLaunchKernelGGL((rar_fused_bf16<0, false>), g, b, 0, st, p);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_sr_step(rar_dtype dt, const StepParams &p, bool first, bool last, bool sgd,
