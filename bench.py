@@ -229,7 +229,7 @@ def secondary_rows(dev, stream, reps=5):
     from ring_all_reduce_amd import api, synth
     rows = []
 
-    def add(name, nbytes, fn, moved=None, extra=None):
+    def add(name, nbytes, fn, moved=None, extra=None, oracle_leg=None):
         total, per, _ = time_launches(fn, reps, 2, stream)
         ms = total / reps
         r = {"row": name, "ms": round(ms, 4), "alg_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -238,6 +238,8 @@ def secondary_rows(dev, stream, reps=5):
             r["moved_GBps"] = round(moved / (ms * 1e-3) / 1e9, 1)
         if extra:
             r.update(extra)
+        if oracle_leg:
+            r.update(oracle_leg())
         rows.append(r)
         log(f"row {name}: {r}")
 
@@ -259,19 +261,21 @@ def secondary_rows(dev, stream, reps=5):
         bufs = synth.rank_gradients(wl, dev)
         w = synth.weights(wl, dev)
         nb = alg_bytes(N, P, 4, True)
+        ring_leg = oracle_timer("ring_f32", bufs, w, wl.lr)
         for algo, an in ((api.FUSED, "fused"), (api.RING, "ring"), (api.NAIVE, "naive_reducer")):
             plan = api.rar_plan(N, P)
             api.rar_plan_set_algo(plan, algo)
             moved = None if algo == api.FUSED else 5 * (N - 1) * P * 4 + 8 * P
+            leg = oracle_timer("naive_f32", bufs, w, wl.lr) if algo == api.NAIVE else ring_leg
             add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream), moved,
-                {"algo": an})
+                {"algo": an}, leg)
         if key == 3:
             wreps = [w] + [w.clone() for _ in range(N - 1)]
             plan = api.rar_plan(N, P)
             moved = 3 * (N - 1) * P * 4 + 8 * P + 2 * (N - 1) * P * 4
             add(f"{wl.name}_reduce_scatter_sgd_allgather", nb,
                 lambda: api.rar_reduce_scatter_sgd_allgather(plan, bufs, wreps, wl.lr, P, stream), moved,
-                {"algo": "rs_sgd_ag"})
+                {"algo": "rs_sgd_ag"}, ring_leg)
             del wreps
         del bufs, w
         torch.cuda.empty_cache()
@@ -282,11 +286,12 @@ def secondary_rows(dev, stream, reps=5):
     bufs = synth.rank_gradients(wl, dev)
     w = synth.weights(wl, dev)
     nb = alg_bytes(N, P, 2, True)
+    bf_leg = oracle_timer("ring_bf16", bufs, w, wl.lr)
     for algo, an in ((api.FUSED, "fused"), (api.RING, "ring")):
         plan = api.rar_plan(N, P, api.BF16)
         api.rar_plan_set_algo(plan, algo)
         add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream), None,
-            {"algo": an})
+            {"algo": an}, bf_leg)
         del plan
     del bufs, w
     torch.cuda.empty_cache()
@@ -301,9 +306,11 @@ def secondary_rows(dev, stream, reps=5):
     bucket_bufs = [torch.empty(mx, dtype=torch.float32, device=dev) for _ in range(wl.N)]
     total = sum(numels)
     nb = alg_bytes(wl.N, total, 4, False)
+    bucket_leg = oracle_timer("buckets_f32", [a[:3 * 6_250_000] for (a, _) in ranks], None, None,
+                              bucket_elems=6_250_000)
     add(f"{wl.name}_pack_reduce_unpack", nb,
         lambda: api.rar_bucket_allreduce_mean(b, tensors, bucket_bufs, api.BALANCED, api.FUSED, stream),
-        3 * nb, {"buckets": nbk})
+        3 * nb, {"buckets": nbk}, bucket_leg)
     # zero-copy: the tensors are views of one flat arena per rank, in backward
     # order, so bucket k is a slice of every arena and needs no packing
     arenas = [flat for (flat, _) in ranks]
@@ -316,8 +323,114 @@ def secondary_rows(dev, stream, reps=5):
     def arena_step():
         for (so, el, _) in infos:
             api.rar_allreduce_mean(plans[el], [a[so:so + el] for a in arenas], el, stream)
-    add(f"{wl.name}_zero_copy_arena", nb, arena_step, None, {"buckets": nbk})
+    add(f"{wl.name}_zero_copy_arena", nb, arena_step, None, {"buckets": nbk}, bucket_leg)
+    del tensors, bucket_bufs
+    rows.append(overlap_row(wl, b, infos, arenas, dev, stream, nb))
+    log(f"row {rows[-1]['row']}: {rows[-1]}")
     return rows
+
+
+def overlap_row(wl, b, infos, arenas, dev, stream, nb, reps=3):
+    """Buckets reduced while a simulated backward pass produces them.
+
+    The producer stream, for each bucket in backward order, runs a bf16
+    matrix product (4096^3, standing in for that bucket's backward compute)
+    and then copies the bucket's gradients into every rank's arena, and
+    records the bucket's ready event; the reduction stream waits for each
+    event in turn (rar_bucket_allreduce_arena).  Reported: producer alone,
+    reduction alone, both together, and the fraction of the reduction time
+    hidden behind the producer."""
+    import torch
+    from ring_all_reduce_amd import api
+    N = len(arenas)
+    pristine = [a.clone() for a in arenas]
+    x = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+    producer, comm = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def produce(events):
+        with torch.cuda.stream(producer):
+            y = x
+            for k, (so, el, _) in enumerate(infos):
+                y = torch.matmul(x, x)
+                for n in range(N):
+                    arenas[n][so:so + el].copy_(pristine[n][so:so + el])
+                if events is not None:
+                    events[k].record(producer)
+        return y
+
+    def timed(run_prod, run_comm):
+        best = None
+        for _ in range(reps):
+            events = [torch.cuda.Event() for _ in infos] if (run_prod and run_comm) else None
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            tp = torch.cuda.Event(enable_timing=True)
+            tc = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            producer.wait_event(t0)
+            comm.wait_event(t0)
+            if run_prod:
+                produce(events)
+            tp.record(producer)
+            if run_comm:
+                api.rar_bucket_allreduce_arena(b, arenas, events, stream=comm)
+            tc.record(comm)
+            torch.cuda.synchronize()
+            ms = max(t0.elapsed_time(tp), t0.elapsed_time(tc))
+            best = ms if best is None else min(best, ms)
+        return best
+
+    t_prod = timed(True, False)
+    t_comm = timed(False, True)
+    t_both = timed(True, True)
+    hidden = (t_prod + t_comm - t_both) / t_comm if t_comm > 0 else 0.0
+    return {"row": f"{wl.name}_overlap_simulated_backward", "buckets": len(infos),
+            "producer_ms": round(t_prod, 3), "allreduce_ms": round(t_comm, 3), "overlapped_ms": round(t_both, 3),
+            "allreduce_alg_GBps": round(nb / (t_comm * 1e-3) / 1e9, 1),
+            "fraction_of_allreduce_hidden": round(hidden, 3),
+            "producer": "per bucket: bf16 4096^3 matmul + copy of the bucket into every arena"}
+
+
+def oracle_timer(kind, bufs, w, lr, sample_elems=20_000_000, bucket_elems=None):
+    """Time the CPU oracle once on a prefix of the row's own inputs (copied to
+    the host); returns a callable giving the row's oracle fields (computed
+    once, shared by the rows of one workload)."""
+    import numpy as np
+    import torch
+    import oracle
+    cache = {}
+
+    def leg():
+        if cache:
+            return cache
+        N = len(bufs)
+        P = min(sample_elems, bufs[0].numel())
+        if kind == "ring_bf16":
+            host = [t[:P].view(torch.int16).cpu().numpy().view(np.uint16).copy() for t in bufs]
+            es = 2
+        else:
+            host = [t[:P].float().cpu().numpy().copy() for t in bufs]
+            es = 4
+        wh = w[:P].cpu().numpy().copy() if w is not None else None
+        t0 = time.perf_counter()
+        if kind == "ring_f32":
+            oracle.ring_allreduce_f32(host, oracle.partition(N, P), wh, lr)
+        elif kind == "naive_f32":
+            oracle.naive_reduce_f32(host, wh, lr)
+        elif kind == "ring_bf16":
+            oracle.ring_allreduce_bf16(host, oracle.partition(N, P, oracle.BALANCED, 2), wh, lr)
+        elif kind == "buckets_f32":
+            for k in range(P // bucket_elems):
+                sl = slice(k * bucket_elems, (k + 1) * bucket_elems)
+                part = [np.ascontiguousarray(h[sl]) for h in host]
+                oracle.ring_allreduce_f32(part, oracle.partition(N, bucket_elems))
+        dt = time.perf_counter() - t0
+        nb = alg_bytes(N, P, es, wh is not None)
+        cache.update({"cpu_oracle_GBps": round(nb / dt / 1e9, 3),
+                      "cpu_oracle_sample": f"{N} ranks x {P} elements ({kind}), {dt:.2f} s, "
+                                           f"{oracle.get_threads()} threads"})
+        return cache
+    return leg
 
 
 # ---------------------------------------------------------------------------

@@ -203,6 +203,22 @@ rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void *const buc
 rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
                                      void *const tensors[], void *const bucket_bufs[], void *stream);
 
+/* Every bucket in order, in place over per-rank flat arenas, each bucket
+ * starting only once its gradients exist ([Gibiansky] §Applying allreduce to
+ * deep learning: back-propagation produces the output layers' gradients
+ * first, so their reduction can overlap the rest of the backward pass).
+ * arenas[n] (device, 16-byte aligned) holds rank n's tensors end to end in
+ * the plan's order, so bucket k is the slice [stream_offset, +elems) of every
+ * arena and needs no packing.  ready_events is a host array of n_buckets
+ * hipEvent_t (as void*), or NULL: before bucket k the call makes `stream`
+ * wait for ready_events[k] (a NULL entry waits for nothing).  The producer
+ * records the events on its own stream; the waits are enqueued, the call
+ * does not block the host.  Every bucket start must be 16-byte aligned
+ * (RAR_EALIGN otherwise; a bucket size that is a multiple of 16 bytes gives
+ * that).  Results are bit-identical to rar_allreduce_mean on each slice. */
+rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
+                                      void *const arenas[], void *const ready_events[], void *stream);
+
 /* ---------------------------------------------------------------------- */
 
 /* Static description of a status code; never NULL. */

@@ -36,6 +36,7 @@ SIGNATURES = {
     "rar_bucket_pack": (_int, [_vp, _int, _int, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]),
     "rar_bucket_unpack": (_int, [_vp, _int, _int, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]),
     "rar_bucket_allreduce_mean": (_int, [_vp, _int, _int, _int, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]),
+    "rar_bucket_allreduce_arena": (_int, [_vp, _int, _int, _int, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp]),
     "rar_strerror": (ctypes.c_char_p, [_int]),
     "rar_version": (_int, []),
 }

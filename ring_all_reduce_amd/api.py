@@ -223,3 +223,16 @@ def rar_bucket_allreduce_mean(b: Buckets, tensors: Sequence[Sequence], bucket_bu
     _check(lib().rar_bucket_allreduce_mean(b.handle, len(tensors), int(chunking), int(algo),
                                            _rank_major(tensors), _ptr_array(bucket_bufs), _stream(stream)),
            "rar_bucket_allreduce_mean")
+
+
+def rar_bucket_allreduce_arena(b: Buckets, arenas: Sequence, ready_events=None, chunking: int = BALANCED,
+                               algo: int = FUSED, stream=None) -> None:
+    """ready_events: None, or one entry per bucket: a torch.cuda.Event, an
+    integer hipEvent_t, or None (no wait)."""
+    ev = None
+    if ready_events is not None:
+        ev = (ctypes.c_void_p * max(len(ready_events), 1))()
+        for i, e in enumerate(ready_events):
+            ev[i] = None if e is None else (e if isinstance(e, int) else int(e.cuda_event)) or None
+    _check(lib().rar_bucket_allreduce_arena(b.handle, len(arenas), int(chunking), int(algo), _ptr_array(arenas),
+                                            ev, _stream(stream)), "rar_bucket_allreduce_arena")

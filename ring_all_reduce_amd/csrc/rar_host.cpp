@@ -576,6 +576,36 @@ extern "C" rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void
     return bucket_copy(b, bucket, N, tensors, bucket_bufs, false, static_cast<hipStream_t>(stream));
 }
 
+namespace {
+
+// Plans for the distinct bucket sizes, made once and kept with the buckets.
+rar_status bucket_plans(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
+                        std::vector<rar_plan_t> &plan_of)
+{
+    const int nb = (int)b->segs.size();
+    plan_of.assign(nb, nullptr);
+    std::lock_guard<std::mutex> lock(b->mu);
+    for (int k = 0; k < nb; ++k) {
+        auto key = std::make_tuple(N, b->elems[k], (int)chunking, (int)algo);
+        auto it = b->plans.find(key);
+        if (it == b->plans.end()) {
+            rar_plan_t pl = nullptr;
+            rar_status rc = rar_plan(N, b->elems[k], b->dtype, chunking, &pl);
+            if (rc == RAR_OK)
+                rc = rar_plan_set_algo(pl, algo);
+            if (rc != RAR_OK) {
+                rar_plan_destroy(pl);
+                return rc;
+            }
+            it = b->plans.emplace(key, pl).first;
+        }
+        plan_of[k] = it->second;
+    }
+    return RAR_OK;
+}
+
+}  // namespace
+
 extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
                                                 void *const tensors[], void *const bucket_bufs[], void *stream)
 {
@@ -587,34 +617,52 @@ extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chun
         if (rc != RAR_OK)
             return rc;
     }
-    // plans for the distinct bucket sizes, made once and kept with the buckets
-    std::vector<rar_plan_t> plan_of(nb, nullptr);
-    {
-        std::lock_guard<std::mutex> lock(b->mu);
-        for (int k = 0; k < nb; ++k) {
-            auto key = std::make_tuple(N, b->elems[k], (int)chunking, (int)algo);
-            auto it = b->plans.find(key);
-            if (it == b->plans.end()) {
-                rar_plan_t pl = nullptr;
-                rar_status rc = rar_plan(N, b->elems[k], b->dtype, chunking, &pl);
-                if (rc == RAR_OK)
-                    rc = rar_plan_set_algo(pl, algo);
-                if (rc != RAR_OK) {
-                    rar_plan_destroy(pl);
-                    return rc;
-                }
-                it = b->plans.emplace(key, pl).first;
-            }
-            plan_of[k] = it->second;
-        }
-    }
+    std::vector<rar_plan_t> plan_of;
+    rar_status rc = bucket_plans(b, N, chunking, algo, plan_of);
+    if (rc != RAR_OK)
+        return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     for (int k = 0; k < nb; ++k) {
-        rar_status rc = bucket_copy(b, k, N, tensors, bucket_bufs, true, st);
+        rc = bucket_copy(b, k, N, tensors, bucket_bufs, true, st);
         if (rc == RAR_OK)
             rc = rar_allreduce_mean(plan_of[k], bucket_bufs, b->elems[k], stream);
         if (rc == RAR_OK)
             rc = bucket_copy(b, k, N, tensors, bucket_bufs, false, st);
+        if (rc != RAR_OK)
+            return rc;
+    }
+    return RAR_OK;
+}
+
+extern "C" rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
+                                                 void *const arenas[], void *const ready_events[], void *stream)
+{
+    if (!b || !arenas || N < 1 || N > kMaxRanks)
+        return RAR_EINVAL;
+    const int es = elem_bytes(b->dtype);
+    const int nb = (int)b->segs.size();
+    for (int n = 0; n < N; ++n) {
+        if (!arenas[n])
+            return RAR_EINVAL;
+        if ((uintptr_t)arenas[n] & 15)
+            return RAR_EALIGN;
+    }
+    for (int k = 0; k < nb; ++k)
+        if ((b->start[k] * es) & 15)
+            return RAR_EALIGN;
+    std::vector<rar_plan_t> plan_of;
+    rar_status rc = bucket_plans(b, N, chunking, algo, plan_of);
+    if (rc != RAR_OK)
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void *slice[kMaxRanks];
+    for (int k = 0; k < nb; ++k) {
+        if (ready_events && ready_events[k] &&
+            hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0) != hipSuccess)
+            return RAR_EHIP;
+        for (int n = 0; n < N; ++n)
+            slice[n] = static_cast<char *>(arenas[n]) + b->start[k] * es;
+        rc = rar_allreduce_mean(plan_of[k], slice, b->elems[k], stream);
         if (rc != RAR_OK)
             return rc;
     }

@@ -154,3 +154,16 @@ def test_bucket_plan_rejects_bad_arguments():
     for args in (([1, -1], 0, 16), ([1], 0, 3), ([1], 5, 16), ([1], 1, 1)):
         with pytest.raises(api.RarError):
             api.rar_bucket_plan(*args)
+
+
+def test_bucket_arena_checks_alignment_and_arguments():
+    L = lib()
+    b = api.rar_bucket_plan([10, 7, 30], api.F32, 12)  # 3-element buckets start at 12-byte multiples
+    ar = api._ptr_array([FAKE, FAKE + (1 << 20)])
+    assert L.rar_bucket_allreduce_arena(b.handle, 2, 0, 0, ar, None, None) == api.EALIGN
+    b16 = api.rar_bucket_plan([10, 7, 30], api.F32, 16)
+    assert L.rar_bucket_allreduce_arena(b16.handle, 2, 0, 0, api._ptr_array([FAKE + 4, FAKE + (1 << 20)]),
+                                        None, None) == api.EALIGN
+    assert L.rar_bucket_allreduce_arena(b16.handle, 2, 0, 0, api._ptr_array([FAKE, 0]), None, None) == api.EINVAL
+    assert L.rar_bucket_allreduce_arena(b16.handle, 0, 0, 0, ar, None, None) == api.EINVAL
+    assert L.rar_bucket_allreduce_arena(None, 2, 0, 0, ar, None, None) == api.EINVAL

@@ -385,3 +385,131 @@ def test_full_size_transformer_buckets_sampled(path):
         _assert_bits(post[0][sl], sub[0], f"bucket at {so}")
         pos += len(idx)
     assert pos == len(all_idx) and total == 735_371_264
+
+
+# ---------------------------------------------------------------------------
+# Largest shapes: element offsets past 2^31, and the maximum rank count
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("algo", [api.FUSED, api.RING])
+def test_offsets_beyond_32_bits_sampled(algo):
+    # 2 ranks x (2^31 + 7) binary32 elements: every byte offset of the second
+    # half of each buffer exceeds 2^32, element offsets exceed 2^31
+    N, P = 2, 2 ** 31 + 7
+    off = oracle.partition(N, P)
+    idx = _samples(off, P, 200_000, 11)
+    idx = np.unique(np.concatenate([idx, np.array([P - 1, P - 2, 2 ** 31 - 1, 2 ** 31, 2 ** 31 + 1])]))
+    idx_d = torch.from_numpy(idx).to(DEV)
+    g = [synth.normal_f32(P, 500 + r, 1.0, DEV) for r in range(N)]
+    w = synth.uniform_f32(P, 599, -0.05, 0.05, DEV)
+    pre = _gather(g, idx_d)
+    wpre = w[idx_d].cpu().numpy()
+    plan = api.rar_plan(N, P)
+    api.rar_plan_set_algo(plan, algo)
+    api.rar_allreduce_sgd(plan, g, w, 0.01, P)
+    torch.cuda.synchronize()
+    assert torch.equal(g[0], g[1])
+    oracle.ring_allreduce_f32(pre, oracle.compact_layout(off, idx), wpre, 0.01)
+    _assert_bits(g[1][idx_d].cpu().numpy(), pre[1], "rank 1 (sampled)")
+    _assert_bits(w[idx_d].cpu().numpy(), wpre, "weights (sampled)")
+
+
+@pytest.mark.parametrize("dt", [api.F32, api.BF16])
+def test_sixty_four_ranks_sampled(dt):
+    N, P = 64, 10_000_019
+    eb = 4 if dt == api.F32 else 2
+    off = oracle.partition(N, P, api.BALANCED, eb)
+    idx = _samples(off, P, 100_000, 12)
+    idx_d = torch.from_numpy(idx).to(DEV)
+    g = [synth.normal_f32(P, 700 + r, 1e-2, DEV) for r in range(N)]
+    if dt == api.BF16:
+        g = [t.to(torch.bfloat16) for t in g]
+    w = synth.uniform_f32(P, 799, -0.05, 0.05, DEV)
+    pre = [_bits16(t[idx_d]) for t in g] if dt == api.BF16 else _gather(g, idx_d)
+    wpre = w[idx_d].cpu().numpy()
+    for algo in (api.FUSED, api.RING):
+        plan = api.rar_plan(N, P, dt)
+        api.rar_plan_set_algo(plan, algo)
+        d = [t.clone() for t in g]
+        wd = w.clone()
+        api.rar_allreduce_sgd(plan, d, wd, 1e-3, P)
+        torch.cuda.synchronize()
+        ref = [x.copy() for x in pre]
+        wr = wpre.copy()
+        if dt == api.BF16:
+            oracle.ring_allreduce_bf16(ref, oracle.compact_layout(off, idx), wr, 1e-3)
+            got = _bits16(d[N - 1][idx_d])
+            assert got.tobytes() == ref[N - 1].tobytes(), f"algo {algo}: first diff {_first_diff(got, ref[N - 1])}"
+        else:
+            oracle.ring_allreduce_f32(ref, oracle.compact_layout(off, idx), wr, 1e-3)
+            _assert_bits(d[N - 1][idx_d].cpu().numpy(), ref[N - 1], f"algo {algo} rank {N - 1}")
+        _assert_bits(wd[idx_d].cpu().numpy(), wr, f"algo {algo} weights")
+        del d, wd
+
+
+# ---------------------------------------------------------------------------
+# Buckets reduced as a simulated backward pass produces them
+# ---------------------------------------------------------------------------
+
+def test_bucket_arena_waits_for_each_ready_event():
+    # The producer stream writes bucket k only after a long matrix product, the
+    # arenas start as NaN, and the reduction runs on another stream: a reduction
+    # that did not wait for bucket k's event would read NaN and fail parity.
+    N = 4
+    specs = synth.transformer_tensors(2, d=128, h=512, V=4000)
+    numels = [s.numel for s in specs]
+    total = sum(numels)
+    bucket_bytes = 4 * 100_000
+    host = [np.random.default_rng(900 + n).standard_normal(total).astype(np.float32) * 1e-3 for n in range(N)]
+    pristine = [torch.from_numpy(h.copy()).to(DEV) for h in host]
+    arenas = [torch.full((total,), float("nan"), device=DEV) for _ in range(N)]
+    b = api.rar_bucket_plan(numels, api.F32, bucket_bytes)
+    nb, _ = api.rar_bucket_count(b)
+    infos = [api.rar_bucket_info(b, k) for k in range(nb)]
+    a = torch.randn(2048, 2048, device=DEV)
+    torch.cuda.synchronize()
+    producer, comm = torch.cuda.Stream(), torch.cuda.Stream()
+    events = []
+    with torch.cuda.stream(producer):
+        for (so, el, _) in infos:
+            a = torch.matmul(a, a) * 1e-3  # stands in for the backward compute of this bucket
+            for n in range(N):
+                arenas[n][so:so + el].copy_(pristine[n][so:so + el])
+            e = torch.cuda.Event()
+            e.record(producer)
+            events.append(e)
+    api.rar_bucket_allreduce_arena(b, arenas, events, stream=comm)
+    comm.synchronize()
+    producer.synchronize()
+    for n in range(1, N):
+        assert torch.equal(arenas[n], arenas[0])
+    got = arenas[0].cpu().numpy()
+    for (so, el, _) in infos:
+        part = [np.ascontiguousarray(h[so:so + el]) for h in host]
+        oracle.ring_allreduce_f32(part, oracle.partition(N, el))
+        _assert_bits(got[so:so + el], part[0], f"bucket at {so}")
+
+
+def test_bucket_arena_without_events_matches_pack_path():
+    N = 3
+    specs = synth.transformer_tensors(1, d=64, h=256, V=1000)
+    numels = [s.numel for s in specs]
+    total = sum(numels)
+    b = api.rar_bucket_plan(numels, api.F32, 4 * 8_000)
+    host = [np.random.default_rng(70 + n).standard_normal(total).astype(np.float32) for n in range(N)]
+    arenas = [torch.from_numpy(h.copy()).to(DEV) for h in host]
+    for algo in (api.FUSED, api.RING):
+        ar = [t.clone() for t in arenas]
+        api.rar_bucket_allreduce_arena(b, ar, None, api.BALANCED, algo)
+        tensors, pos = [[] for _ in range(N)], 0
+        flat = [t.clone() for t in arenas]
+        for s in specs:
+            for n in range(N):
+                tensors[n].append(flat[n][pos:pos + s.numel])
+            pos += s.numel
+        _, mx = api.rar_bucket_count(b)
+        bufs = [torch.empty(mx, device=DEV) for _ in range(N)]
+        api.rar_bucket_allreduce_mean(b, tensors, bufs, api.BALANCED, algo)
+        torch.cuda.synchronize()
+        for n in range(N):
+            assert torch.equal(ar[n], flat[n])
