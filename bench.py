@@ -308,9 +308,15 @@ def secondary_rows(dev, stream, reps=5):
     nb = alg_bytes(wl.N, total, 4, False)
     bucket_leg = oracle_timer("buckets_f32", [a[:3 * 6_250_000] for (a, _) in ranks], None, None,
                               bucket_elems=6_250_000)
-    add(f"{wl.name}_pack_reduce_unpack", nb,
-        lambda: api.rar_bucket_allreduce_mean(b, tensors, bucket_bufs, api.BALANCED, api.FUSED, stream),
-        3 * nb, {"buckets": nbk}, bucket_leg)
+    # straight from the tensor lists: each bucket's segments cut at its chunk boundaries
+    add(f"{wl.name}_tensor_lists_direct", nb,
+        lambda: api.rar_bucket_allreduce_mean(b, tensors, None, api.BALANCED, api.FUSED, stream),
+        None, {"buckets": nbk}, bucket_leg)
+    # ring steps per bucket: pack into bucket buffers, 2(N-1) steps, unpack
+    moved_ring = 2 * (2 * wl.N * total * 4) + 5 * (wl.N - 1) * total * 4
+    add(f"{wl.name}_pack_ring_unpack", nb,
+        lambda: api.rar_bucket_allreduce_mean(b, tensors, bucket_bufs, api.BALANCED, api.RING, stream),
+        moved_ring, {"buckets": nbk, "algo": "ring"}, bucket_leg)
     # zero-copy: the tensors are views of one flat arena per rank, in backward
     # order, so bucket k is a slice of every arena and needs no packing
     arenas = [flat for (flat, _) in ranks]

@@ -34,10 +34,11 @@
  * Memory and streams: every device pointer is owned by the caller and must
  * stay valid until the work enqueued on `stream` (a hipStream_t passed as
  * void*, NULL = the default stream) has finished.  Calls return after
- * enqueueing; they never synchronise.  Device pointers must be 16-byte
- * aligned.  No call allocates device memory except rar_plan_set_algo for a
- * bf16 ring plan (its binary32 workspace) and rar_bucket_allreduce_mean
- * (nothing: it takes the caller's bucket buffers).
+ * enqueueing; they never synchronise.  Rank buffers, weights and bucket
+ * buffers must be 16-byte aligned; bucket tensors need only element
+ * alignment.  The only device allocation is the binary32 workspace of a
+ * bf16 plan set to RAR_ALGO_RING (rar_plan_set_algo, or a bucket call that
+ * builds such a plan for itself); it lives until the plan is destroyed.
  *
  * Errors: every argument is checked before any device work is enqueued; on
  * error nothing is enqueued and a negative rar_status is returned.
@@ -195,11 +196,15 @@ rar_status rar_bucket_pack(rar_buckets_t b, int bucket, int N, void *const tenso
 rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void *const bucket_bufs[],
                              void *const tensors[], void *stream);
 
-/* Every bucket in order: pack, all-reduce-mean (plan built inside for the
- * bucket's size with `chunking` and `algo`), unpack.  bucket_bufs[n] are N
- * device buffers of at least max_bucket_elems elements, reused by every
- * bucket.  Element e of a bucket ends bit-identical to what
- * rar_allreduce_mean gives for that bucket alone. */
+/* Every bucket in order, all-reduce-mean in place in the tensors.  Element e
+ * of a bucket ends bit-identical to what rar_allreduce_mean gives for that
+ * bucket alone (chunk table of the bucket's size, `chunking`).
+ * With RAR_ALGO_FUSED and N in {2, 4, 8, 10, 16, 40} the reduction reads and
+ * writes the tensors directly (each bucket segment cut at the bucket's chunk
+ * boundaries; 2*N*size bytes moved per bucket) and bucket_bufs may be NULL.
+ * Otherwise each bucket is packed into bucket_bufs[n] (N device buffers of at
+ * least max_bucket_elems elements, 16-byte aligned, reused by every bucket),
+ * reduced with `algo`, and unpacked. */
 rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
                                      void *const tensors[], void *const bucket_bufs[], void *stream);
 

@@ -218,10 +218,13 @@ def rar_bucket_unpack(b: Buckets, bucket: int, bucket_bufs: Sequence, tensors: S
                                    _rank_major(tensors), _stream(stream)), "rar_bucket_unpack")
 
 
-def rar_bucket_allreduce_mean(b: Buckets, tensors: Sequence[Sequence], bucket_bufs: Sequence,
+def rar_bucket_allreduce_mean(b: Buckets, tensors: Sequence[Sequence], bucket_bufs=None,
                               chunking: int = BALANCED, algo: int = FUSED, stream=None) -> None:
+    """bucket_bufs: N buffers of max_bucket_elems, or None when the reduction
+    runs straight from the tensors (RAR_ALGO_FUSED at a supported rank count)."""
+    bufs = None if bucket_bufs is None else _ptr_array(bucket_bufs)
     _check(lib().rar_bucket_allreduce_mean(b.handle, len(tensors), int(chunking), int(algo),
-                                           _rank_major(tensors), _ptr_array(bucket_bufs), _stream(stream)),
+                                           _rank_major(tensors), bufs, _stream(stream)),
            "rar_bucket_allreduce_mean")
 
 

@@ -505,15 +505,17 @@ extern "C" rar_status rar_bucket_segment(rar_buckets_t b, int bucket, int seg, i
 
 namespace {
 
-rar_status check_bucket_args(rar_buckets_t b, int bucket, int N, void *const tensors[], void *const bucket_bufs[])
+rar_status check_bucket_args(rar_buckets_t b, int bucket, int N, void *const tensors[], void *const bucket_bufs[],
+                             bool need_bufs = true)
 {
-    if (!b || bucket < 0 || bucket >= (int)b->segs.size() || N < 1 || N > kMaxRanks || !tensors || !bucket_bufs)
+    if (!b || bucket < 0 || bucket >= (int)b->segs.size() || N < 1 || N > kMaxRanks || !tensors ||
+        (need_bufs && !bucket_bufs))
         return RAR_EINVAL;
     const int es = elem_bytes(b->dtype);
     for (int n = 0; n < N; ++n) {
-        if (!bucket_bufs[n])
+        if (bucket_bufs && !bucket_bufs[n])
             return RAR_EINVAL;
-        if ((uintptr_t)bucket_bufs[n] & 15)
+        if (bucket_bufs && ((uintptr_t)bucket_bufs[n] & 15))
             return RAR_EALIGN;
         for (const Segment &s : b->segs[bucket]) {
             const void *t = tensors[(int64_t)n * b->n_tensors + s.tensor];
@@ -606,14 +608,59 @@ rar_status bucket_plans(rar_buckets_t b, int N, rar_chunking chunking, rar_algo 
 
 }  // namespace
 
+namespace {
+
+// Bucket k reduced in place in the tensors: each segment is cut at the
+// bucket's chunk boundaries into jobs with a uniform fold start.
+rar_status bucket_direct(rar_buckets_t b, int k, int N, const rar_plan_s *pl, void *const tensors[], hipStream_t st)
+{
+    const int es = elem_bytes(b->dtype);
+    const int per_launch = std::min(rar::kMaxJobs, rar::kMaxJobPtrs / N);
+    rar::JobsParams jp{};
+    int64_t max_len = 0;
+    auto flush = [&]() -> rar_status {
+        hipError_t e = rar::launch_bucket_jobs(b->dtype, N, jp, block_budget(pl), max_len, st);
+        jp.njobs = 0;
+        max_len = 0;
+        return hip_status(e);
+    };
+    for (const Segment &sg : b->segs[k]) {
+        for (int c = 0; c < N; ++c) {
+            const int64_t lo = std::max(sg.boff, pl->ct.off[c]);
+            const int64_t hi = std::min(sg.boff + sg.len, pl->ct.off[c + 1]);
+            if (hi <= lo)
+                continue;
+            const int j = jp.njobs;
+            bool same_align = true;
+            for (int n = 0; n < N; ++n) {
+                char *t = static_cast<char *>(tensors[(int64_t)n * b->n_tensors + sg.tensor]);
+                jp.ptr[j * N + n] = t + (sg.toff + (lo - sg.boff)) * es;
+                same_align &= (((uintptr_t)jp.ptr[j * N + n] ^ (uintptr_t)jp.ptr[j * N]) & 15) == 0;
+            }
+            jp.job[j] = {hi - lo, c, same_align ? 1 : 0};
+            jp.njobs = j + 1;
+            max_len = std::max(max_len, hi - lo);
+            if (jp.njobs == per_launch) {
+                rar_status rc = flush();
+                if (rc != RAR_OK)
+                    return rc;
+            }
+        }
+    }
+    return jp.njobs ? flush() : RAR_OK;
+}
+
+}  // namespace
+
 extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
                                                 void *const tensors[], void *const bucket_bufs[], void *stream)
 {
     if (!b)
         return RAR_EINVAL;
     const int nb = (int)b->segs.size();
+    const bool direct = algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N);
     for (int k = 0; k < nb; ++k) {
-        rar_status rc = check_bucket_args(b, k, N, tensors, bucket_bufs);
+        rar_status rc = check_bucket_args(b, k, N, tensors, bucket_bufs, !direct);
         if (rc != RAR_OK)
             return rc;
     }
@@ -622,6 +669,14 @@ extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chun
     if (rc != RAR_OK)
         return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (direct) {
+        for (int k = 0; k < nb; ++k) {
+            rc = bucket_direct(b, k, N, plan_of[k], tensors, st);
+            if (rc != RAR_OK)
+                return rc;
+        }
+        return RAR_OK;
+    }
     for (int k = 0; k < nb; ++k) {
         rc = bucket_copy(b, k, N, tensors, bucket_bufs, true, st);
         if (rc == RAR_OK)

@@ -57,6 +57,24 @@ struct CopyParams {
     int unit;  // element size in bytes (2 or 4) for unaligned remainders
 };
 
+// One job of a bucket reduced straight from the tensors: `len` elements whose
+// fold starts at rank c; vec_ok == 0 when the ranks' pointers differ in their
+// 16-byte alignment (scalar path).
+struct JobDesc {
+    int64_t len;
+    int32_t c;
+    int32_t vec_ok;
+};
+
+constexpr int kMaxJobs = 48;
+constexpr int kMaxJobPtrs = 320;
+
+struct JobsParams {
+    void *ptr[kMaxJobPtrs];  // job j, rank r: ptr[j*N + r]
+    JobDesc job[kMaxJobs];
+    int njobs;
+};
+
 // Single reducer (prior art): rank 0 accumulates rank `src`.
 struct PairParams {
     RankPtrs bufs;
@@ -74,5 +92,9 @@ hipError_t launch_sr_step(rar_dtype dt, const StepParams &p, bool first, bool la
                           int max_blocks, int64_t max_chunk, hipStream_t st);
 hipError_t launch_copy(const CopyParams &p, int max_blocks, int64_t max_job_bytes, hipStream_t st);
 hipError_t launch_pair_add(const PairParams &p, bool last, bool sgd, int max_blocks, hipStream_t st);
+// Rank counts with a bucket-jobs kernel (others use pack, reduce, unpack).
+bool bucket_jobs_supported(int N);
+hipError_t launch_bucket_jobs(rar_dtype dt, int N, const JobsParams &p, int max_blocks, int64_t max_len,
+                              hipStream_t st);
 
 }  // namespace rar

@@ -374,27 +374,16 @@ __global__ __launch_bounds__(kThreads) void rar_fused_bf16(FusedParams p)
 // faster that way (measured on MI355X, 10 ranks x 300M with SGD: ~5.45 TB/s
 // with one group, ~5.75 TB/s with two to four).
 
-// Scalar path for the at most VEC-1 elements before the first and after the
-// last aligned 16-byte group of a chunk (block 0 of the chunk, lanes < 2*VEC).
-template <typename T, int VEC, int NT, bool SGD>
-__device__ __forceinline__ void fused_head_tail(const FusedParams &p, int c, int64_t e0, int64_t e1,
-                                                int64_t a0, int64_t a1)
+// Scalar path for one element e of a span: the whole fold in one lane.
+// base(r) is rank r's element pointer at the span's element 0.
+template <typename T, int NT, bool SGD, class Base>
+__device__ __forceinline__ void span_elem(Base base, float *w, float lr, int c, int64_t e)
 {
-    if (blockIdx.x != 0 || threadIdx.x >= 2 * VEC)
-        return;
-    const int t = threadIdx.x;
-    int64_t e = -1;
-    if (t < a0 - e0)
-        e = e0 + t;
-    else if (t >= VEC && t < VEC + (e1 - a1))
-        e = a1 + (t - VEC);
-    if (e < 0)
-        return;
     auto val = [&](int r) -> float {
         if constexpr (sizeof(T) == 4)
-            return static_cast<const float *>(p.bufs.p[r])[e];
+            return base(r)[e];
         else
-            return bf16_one(static_cast<const uint16_t *>(p.bufs.p[r])[e]);
+            return bf16_one(base(r)[e]);
     };
     float acc = val(c);
     int r = c;
@@ -405,41 +394,56 @@ __device__ __forceinline__ void fused_head_tail(const FusedParams &p, int c, int
     const float m = acc / (float)NT;
     for (int n = 0; n < NT; ++n) {
         if constexpr (sizeof(T) == 4)
-            static_cast<float *>(p.bufs.p[n])[e] = m;
+            base(n)[e] = m;
         else
-            static_cast<uint16_t *>(p.bufs.p[n])[e] = (uint16_t)bf16_rne(m);
+            base(n)[e] = (uint16_t)bf16_rne(m);
     }
     if (SGD) {
-        const float step = p.lr * m;
-        p.w[e] = p.w[e] - step;
+        const float step = lr * m;
+        w[e] = w[e] - step;
     }
 }
 
-template <int NT, int G, bool SGD>
-__global__ __launch_bounds__(kThreads *G) void rar_fused_f32_grp(FusedParams p)
+// Head and tail of a span: the elements before the first 16-byte aligned
+// address of base(0) (every rank's base shares that alignment) and after the
+// last whole 16-byte group.  Block bx == 0, lanes < 2*VEC.  Returns the head
+// length h and the number of whole vectors nvec.
+template <typename T, int NT, bool SGD, class Base>
+__device__ __forceinline__ void span_head_tail(Base base, float *w, float lr, int c, int64_t len, int64_t bx,
+                                               int64_t &h, int64_t &nvec)
+{
+    constexpr int VEC = 16 / sizeof(T);
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(base(0));
+    h = (int64_t)(((16 - (addr & 15)) & 15) / sizeof(T));
+    if (h > len)
+        h = len;
+    nvec = (len - h) / VEC;
+    const int64_t tail0 = h + nvec * VEC;
+    if (bx != 0 || threadIdx.x >= 2 * VEC)
+        return;
+    const int64_t t = threadIdx.x;
+    if (t < h)
+        span_elem<T, NT, SGD>(base, w, lr, c, t);
+    else if (t >= VEC && t - VEC < len - tail0)
+        span_elem<T, NT, SGD>(base, w, lr, c, tail0 + (t - VEC));
+}
+
+// The grouped body over one binary32 span of `len` elements whose fold starts
+// at rank c; tiles bx, bx+gx, ... of the aligned part.
+template <int NT, int G, bool SGD, class Base>
+__device__ __forceinline__ void grouped_span_f32(Base base, float *w, float lr, int c, int64_t len, int64_t bx,
+                                                 int64_t gx, f32x4 *chain, f32x4 *mean)
 {
     static_assert(NT > 0 && G >= 1, "compile-time rank count");
     constexpr int PER = (NT + G - 1) / G;
-    const int c = blockIdx.y;
     const int g = threadIdx.x / kThreads;
     const int lane = threadIdx.x % kThreads;
     const int k0 = g * PER;
     const int cnt = k0 >= NT ? 0 : (NT - k0 < PER ? NT - k0 : PER);
-    __shared__ f32x4 chain[G > 1 ? kThreads : 1];
-    __shared__ f32x4 mean[G > 1 ? kThreads : 1];
-
-    const int64_t e0 = p.ct.off[c], e1 = p.ct.off[c + 1];
-    if (e1 <= e0)
-        return;
-    int64_t a0 = (e0 + 3) / 4 * 4, a1 = e1 / 4 * 4;
-    if (a0 > a1) {
-        a0 = e1;
-        a1 = e1;
-    }
-    fused_head_tail<float, 4, NT, SGD>(p, c, e0, e1, a0, a1);
-    const int64_t nvec = (a1 - a0) / 4;
+    int64_t h, nvec;
+    span_head_tail<float, NT, SGD>(base, w, lr, c, len, bx, h, nvec);
     const int64_t ntiles = (nvec + kThreads - 1) / kThreads;
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    for (int64_t t = bx; t < ntiles; t += gx) {
         const int64_t v = t * kThreads + lane;
         const bool ok = v < nvec;
         f32x4 x[PER];
@@ -450,11 +454,11 @@ __global__ __launch_bounds__(kThreads *G) void rar_fused_f32_grp(FusedParams p)
                 if (j < cnt) {
                     int r = c + k0 + j;
                     r = r >= NT ? r - NT : r;
-                    x[j] = ld(vec_at<const f32x4, const float>(p.bufs.p[r], a0) + v);
+                    x[j] = ld(reinterpret_cast<const f32x4 *>(base(r) + h) + v);
                 }
             }
             if (SGD && g == G - 1)
-                wv = ld(vec_at<const f32x4, const float>(p.w, a0) + v);
+                wv = ld(reinterpret_cast<const f32x4 *>(w + h) + v);
         }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (g == 0 && ok) {
@@ -467,11 +471,11 @@ __global__ __launch_bounds__(kThreads *G) void rar_fused_f32_grp(FusedParams p)
         f32x4 m;
         if constexpr (G > 1) {
 #pragma unroll
-            for (int h = 1; h < G; ++h) {
-                if (g == h - 1)
+            for (int hop = 1; hop < G; ++hop) {
+                if (g == hop - 1)
                     chain[lane] = acc;
                 __syncthreads();
-                if (g == h && ok) {
+                if (g == hop && ok) {
                     acc = chain[lane];
 #pragma unroll
                     for (int j = 0; j < PER; ++j)
@@ -492,43 +496,34 @@ __global__ __launch_bounds__(kThreads *G) void rar_fused_f32_grp(FusedParams p)
                 if (j < cnt) {
                     int r = c + k0 + j;
                     r = r >= NT ? r - NT : r;
-                    st(vec_at<f32x4, float>(p.bufs.p[r], a0) + v, m);
+                    st(reinterpret_cast<f32x4 *>(base(r) + h) + v, m);
                 }
             }
             if (SGD && g == G - 1) {
-                const f32x4 step = p.lr * m;
+                const f32x4 step = lr * m;
                 wv = wv - step;
-                st(vec_at<f32x4, float>(p.w, a0) + v, wv);
+                st(reinterpret_cast<f32x4 *>(w + h) + v, wv);
             }
         }
     }
 }
 
-template <int NT, int G, bool SGD>
-__global__ __launch_bounds__(kThreads *G) void rar_fused_bf16_grp(FusedParams p)
+// The same over a bf16 span (eight elements per 16-byte vector, binary32
+// partial sums of 32 bytes per lane).
+template <int NT, int G, bool SGD, class Base>
+__device__ __forceinline__ void grouped_span_bf16(Base base, float *w, float lr, int c, int64_t len, int64_t bx,
+                                                  int64_t gx, f32x4 *chain, f32x4 *mean)
 {
     static_assert(NT > 0 && G >= 1, "compile-time rank count");
     constexpr int PER = (NT + G - 1) / G;
-    const int c = blockIdx.y;
     const int g = threadIdx.x / kThreads;
     const int lane = threadIdx.x % kThreads;
     const int k0 = g * PER;
     const int cnt = k0 >= NT ? 0 : (NT - k0 < PER ? NT - k0 : PER);
-    __shared__ f32x4 chain[G > 1 ? 2 * kThreads : 1];
-    __shared__ f32x4 mean[G > 1 ? 2 * kThreads : 1];
-
-    const int64_t e0 = p.ct.off[c], e1 = p.ct.off[c + 1];
-    if (e1 <= e0)
-        return;
-    int64_t a0 = (e0 + 7) / 8 * 8, a1 = e1 / 8 * 8;
-    if (a0 > a1) {
-        a0 = e1;
-        a1 = e1;
-    }
-    fused_head_tail<uint16_t, 8, NT, SGD>(p, c, e0, e1, a0, a1);
-    const int64_t nvec = (a1 - a0) / 8;
+    int64_t h, nvec;
+    span_head_tail<uint16_t, NT, SGD>(base, w, lr, c, len, bx, h, nvec);
     const int64_t ntiles = (nvec + kThreads - 1) / kThreads;
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    for (int64_t t = bx; t < ntiles; t += gx) {
         const int64_t v = t * kThreads + lane;
         const bool ok = v < nvec;
         u32x4 x[PER];
@@ -539,11 +534,11 @@ __global__ __launch_bounds__(kThreads *G) void rar_fused_bf16_grp(FusedParams p)
                 if (j < cnt) {
                     int r = c + k0 + j;
                     r = r >= NT ? r - NT : r;
-                    x[j] = ld(vec_at<const u32x4, const uint16_t>(p.bufs.p[r], a0) + v);
+                    x[j] = ld(reinterpret_cast<const u32x4 *>(base(r) + h) + v);
                 }
             }
             if (SGD && g == G - 1) {
-                const f32x4 *wp = vec_at<const f32x4, const float>(p.w, a0);
+                const f32x4 *wp = reinterpret_cast<const f32x4 *>(w + h);
                 w0 = ld(wp + 2 * v);
                 w1 = ld(wp + 2 * v + 1);
             }
@@ -564,13 +559,13 @@ __global__ __launch_bounds__(kThreads *G) void rar_fused_bf16_grp(FusedParams p)
         f32x4 mlo, mhi;
         if constexpr (G > 1) {
 #pragma unroll
-            for (int h = 1; h < G; ++h) {
-                if (g == h - 1) {
+            for (int hop = 1; hop < G; ++hop) {
+                if (g == hop - 1) {
                     chain[2 * lane] = lo;
                     chain[2 * lane + 1] = hi;
                 }
                 __syncthreads();
-                if (g == h && ok) {
+                if (g == hop && ok) {
                     lo = chain[2 * lane];
                     hi = chain[2 * lane + 1];
 #pragma unroll
@@ -602,18 +597,80 @@ __global__ __launch_bounds__(kThreads *G) void rar_fused_bf16_grp(FusedParams p)
                 if (j < cnt) {
                     int r = c + k0 + j;
                     r = r >= NT ? r - NT : r;
-                    st(vec_at<u32x4, uint16_t>(p.bufs.p[r], a0) + v, out);
+                    st(reinterpret_cast<u32x4 *>(base(r) + h) + v, out);
                 }
             }
             if (SGD && g == G - 1) {
-                f32x4 *wp = vec_at<f32x4, float>(p.w, a0);
-                const f32x4 s0 = p.lr * mlo, s1 = p.lr * mhi;
+                f32x4 *wp = reinterpret_cast<f32x4 *>(w + h);
+                const f32x4 s0 = lr * mlo, s1 = lr * mhi;
                 w0 = w0 - s0;
                 w1 = w1 - s1;
                 st(wp + 2 * v, w0);
                 st(wp + 2 * v + 1, w1);
             }
         }
+    }
+}
+
+// Flat rank buffers: span = chunk c = blockIdx.y of the chunk table.
+template <int NT, int G, bool SGD>
+__global__ __launch_bounds__(kThreads *G) void rar_fused_f32_grp(FusedParams p)
+{
+    __shared__ f32x4 chain[G > 1 ? kThreads : 1];
+    __shared__ f32x4 mean[G > 1 ? kThreads : 1];
+    const int c = blockIdx.y;
+    const int64_t e0 = p.ct.off[c], e1 = p.ct.off[c + 1];
+    if (e1 <= e0)
+        return;
+    auto base = [&](int r) { return static_cast<float *>(p.bufs.p[r]) + e0; };
+    grouped_span_f32<NT, G, SGD>(base, SGD ? p.w + e0 : nullptr, p.lr, c, e1 - e0, blockIdx.x, gridDim.x, chain,
+                                 mean);
+}
+
+template <int NT, int G, bool SGD>
+__global__ __launch_bounds__(kThreads *G) void rar_fused_bf16_grp(FusedParams p)
+{
+    __shared__ f32x4 chain[G > 1 ? 2 * kThreads : 1];
+    __shared__ f32x4 mean[G > 1 ? 2 * kThreads : 1];
+    const int c = blockIdx.y;
+    const int64_t e0 = p.ct.off[c], e1 = p.ct.off[c + 1];
+    if (e1 <= e0)
+        return;
+    auto base = [&](int r) { return static_cast<uint16_t *>(p.bufs.p[r]) + e0; };
+    grouped_span_bf16<NT, G, SGD>(base, SGD ? p.w + e0 : nullptr, p.lr, c, e1 - e0, blockIdx.x, gridDim.x, chain,
+                                  mean);
+}
+
+// ---------------------------------------------------------------------------
+// Buckets straight from the tensor lists.
+// ---------------------------------------------------------------------------
+//
+// A bucket is a run of tensor segments cut into N chunks; a job is the part
+// of one segment inside one chunk, so its fold starts at that chunk's rank
+// and every rank's elements of the job are contiguous in that rank's tensor.
+// Job j of rank r starts at ptr[j*N + r].  The same grouped body reduces each
+// job in place in the tensors: no packing into bucket buffers and back, so a
+// bucket moves 2*N*size bytes instead of 6*N*size.  vec_ok = 0 marks a job
+// whose ranks' pointers differ in their 16-byte alignment; it goes through
+// the scalar path.
+template <typename T, int NT, int G>
+__global__ __launch_bounds__(kThreads *G) void rar_bucket_jobs(JobsParams p)
+{
+    constexpr int SLOT = sizeof(T) == 4 ? 1 : 2;
+    __shared__ f32x4 chain[G > 1 ? SLOT * kThreads : 1];
+    __shared__ f32x4 mean[G > 1 ? SLOT * kThreads : 1];
+    const int j = blockIdx.y;
+    const JobDesc jd = p.job[j];
+    auto base = [&](int r) { return static_cast<T *>(p.ptr[j * NT + r]); };
+    if (jd.vec_ok) {
+        if constexpr (sizeof(T) == 4)
+            grouped_span_f32<NT, G, false>(base, nullptr, 0.f, jd.c, jd.len, blockIdx.x, gridDim.x, chain, mean);
+        else
+            grouped_span_bf16<NT, G, false>(base, nullptr, 0.f, jd.c, jd.len, blockIdx.x, gridDim.x, chain, mean);
+    } else {
+        for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < jd.len;
+             e += (int64_t)gridDim.x * blockDim.x)
+            span_elem<T, NT, false>(base, nullptr, 0.f, jd.c, e);
     }
 }
 
@@ -937,7 +994,43 @@ hipError_t fused_grouped(rar_dtype dt, const FusedParams &p, int max_blocks, int
     return hipGetLastError();
 }
 
+template <int NT>
+hipError_t bucket_jobs_n(rar_dtype dt, const JobsParams &p, int max_blocks, int64_t max_len, hipStream_t st)
+{
+    if (dt == RAR_F32) {
+        constexpr int G = groups_f32(NT);
+        const dim3 g(blocks_x(max_blocks, p.njobs, max_len / 4 + 1, 1), p.njobs), b(kThreads * G);
+        hipLaunchKernelGGL((rar_bucket_jobs<float, NT, G>), g, b, 0, st, p);
+    } else {
+        constexpr int G = groups_bf16(NT);
+        const dim3 g(blocks_x(max_blocks, p.njobs, max_len / 8 + 1, 1), p.njobs), b(kThreads * G);
+        hipLaunchKernelGGL((rar_bucket_jobs<uint16_t, NT, G>), g, b, 0, st, p);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool bucket_jobs_supported(int N)
+{
+    return N == 2 || N == 4 || N == 8 || N == 10 || N == 16 || N == 40;
+}
+
+hipError_t launch_bucket_jobs(rar_dtype dt, int N, const JobsParams &p, int max_blocks, int64_t max_len,
+                              hipStream_t st)
+{
+    if (p.njobs <= 0)
+        return hipSuccess;
+    switch (N) {
+    case 2: return bucket_jobs_n<2>(dt, p, max_blocks, max_len, st);
+    case 4: return bucket_jobs_n<4>(dt, p, max_blocks, max_len, st);
+    case 8: return bucket_jobs_n<8>(dt, p, max_blocks, max_len, st);
+    case 10: return bucket_jobs_n<10>(dt, p, max_blocks, max_len, st);
+    case 16: return bucket_jobs_n<16>(dt, p, max_blocks, max_len, st);
+    case 40: return bucket_jobs_n<40>(dt, p, max_blocks, max_len, st);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 // Rank counts with a compile-time kernel (the workloads' 4, 8, 10 and 40, and
 // the powers of two up to 16) take the grouped kernels; any other N takes the

@@ -342,7 +342,7 @@ def test_full_size_40_rank_bf16_sampled(algo):
     assert np.max(np.abs(y - exact)) / np.max(np.abs(exact)) <= 1e-2
 
 
-@pytest.mark.parametrize("path", ["pack", "arena"])
+@pytest.mark.parametrize("path", ["tensors", "arena", "tensors_ring"])
 def test_full_size_transformer_buckets_sampled(path):
     wl = synth.WORKLOADS[4]
     N = wl.N
@@ -364,9 +364,11 @@ def test_full_size_transformer_buckets_sampled(path):
     all_idx = np.concatenate([so + idx for (so, _, _, idx) in per_bucket])
     idx_d = torch.from_numpy(all_idx).to(DEV)
     pre = _gather(arenas, idx_d)
-    if path == "pack":
+    if path == "tensors":  # straight from the tensor lists, no bucket buffers
+        api.rar_bucket_allreduce_mean(b, tensors, None)
+    elif path == "tensors_ring":  # pack, ring steps, unpack
         bufs = [torch.empty(mx, device=DEV) for _ in range(N)]
-        api.rar_bucket_allreduce_mean(b, tensors, bufs)
+        api.rar_bucket_allreduce_mean(b, tensors, bufs, api.BALANCED, api.RING)
     else:
         plans = {}
         for (so, el, _, _) in per_bucket:
@@ -513,3 +515,82 @@ def test_bucket_arena_without_events_matches_pack_path():
         torch.cuda.synchronize()
         for n in range(N):
             assert torch.equal(ar[n], flat[n])
+
+
+@pytest.mark.parametrize("algo", [api.FUSED, api.RING])
+def test_bucketed_bf16_small_transformer_bit_exact(algo):
+    N = 5
+    specs = synth.transformer_tensors(1, d=64, h=256, V=777)
+    numels = [s.numel for s in specs]
+    bucket_bytes = 2 * 30_000
+    host = [[synth.student_t3_bf16(s.numel, 3000 + 100 * n + t, 1e-3, "cpu").view(torch.int16).numpy()
+             .view(np.uint16).copy() for t, s in enumerate(specs)] for n in range(N)]
+    tensors = [[torch.from_numpy(x.view(np.int16).copy()).to(DEV).view(torch.bfloat16) for x in rank]
+               for rank in host]
+    b = api.rar_bucket_plan(numels, api.BF16, bucket_bytes)
+    nb, mx = api.rar_bucket_count(b)
+    bufs = [torch.empty(mx, dtype=torch.bfloat16, device=DEV) for _ in range(N)]
+    api.rar_bucket_allreduce_mean(b, tensors, bufs, api.BALANCED, algo)
+    torch.cuda.synchronize()
+    layout = oracle.bucket_layout(numels, 2, bucket_bytes)
+    assert len(layout) == nb
+    for segs in layout:
+        size = sum(s[3] for s in segs)
+        part = [np.concatenate([host[n][t][toff:toff + ln] for (t, toff, _, ln) in segs]) for n in range(N)]
+        oracle.ring_allreduce_bf16(part, oracle.partition(N, size, oracle.BALANCED, 2))
+        for n in (0, N - 1):
+            got = np.concatenate([_bits16(tensors[n][t][toff:toff + ln]) for (t, toff, _, ln) in segs])
+            assert got.tobytes() == part[n].tobytes(), f"rank {n}: first diff {_first_diff(got, part[n])}"
+
+
+@pytest.mark.parametrize("skew", ["same", "different"])
+@pytest.mark.parametrize("dt", [api.F32, api.BF16])
+def test_bucket_tensors_direct_with_misaligned_views(skew, dt):
+    # Tensors are views at odd element offsets: with the same offset on every
+    # rank the direct path runs vector bodies with scalar heads and tails; with
+    # different offsets per rank it runs the scalar path.  Both must match the
+    # oracle bit for bit.
+    N = 4
+    tdt = torch.float32 if dt == api.F32 else torch.bfloat16
+    es = 4 if dt == api.F32 else 2
+    numels = [5, 1000, 3, 4097, 77, 20_000, 1]
+    total = sum(numels)
+    bucket_bytes = es * 3001
+    rng = np.random.default_rng(5)
+    if dt == api.F32:
+        host = [rng.standard_normal(total).astype(np.float32) for _ in range(N)]
+    else:
+        host = [oracle.f32_to_bf16(rng.standard_normal(total).astype(np.float32) * 1e-2) for _ in range(N)]
+    tensors, keep = [], []
+    for n in range(N):
+        shift = 1 if skew == "same" else 1 + n
+        arena = torch.zeros(total + 16, dtype=tdt, device=DEV)
+        src = torch.from_numpy(host[n].view(np.int16) if dt == api.BF16 else host[n]).to(DEV)
+        arena[shift:shift + total].copy_(src.view(tdt) if dt == api.BF16 else src)
+        keep.append(arena)
+        ts, pos = [], shift
+        for k in numels:
+            ts.append(arena[pos:pos + k])
+            pos += k
+        tensors.append(ts)
+    b = api.rar_bucket_plan(numels, dt, bucket_bytes)
+    api.rar_bucket_allreduce_mean(b, tensors, None)
+    torch.cuda.synchronize()
+    layout = oracle.bucket_layout(numels, es, bucket_bytes)
+    stream = [h.copy() for h in host]
+    pos = 0
+    for segs in layout:
+        size = sum(sg[3] for sg in segs)
+        part = [np.ascontiguousarray(h[pos:pos + size]) for h in stream]
+        if dt == api.F32:
+            oracle.ring_allreduce_f32(part, oracle.partition(N, size))
+        else:
+            oracle.ring_allreduce_bf16(part, oracle.partition(N, size, oracle.BALANCED, 2))
+        for n in range(N):
+            stream[n][pos:pos + size] = part[n]
+        pos += size
+    for n in range(N):
+        shift = 1 if skew == "same" else 1 + n
+        got = keep[n][shift:shift + total]
+        got = _bits16(got) if dt == api.BF16 else got.cpu().numpy()
+        assert got.tobytes() == stream[n].tobytes(), f"rank {n}: first diff {_first_diff(got, stream[n])}"
