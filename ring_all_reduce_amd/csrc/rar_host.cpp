@@ -525,6 +525,19 @@ rar_status check_bucket_args(rar_buckets_t b, int bucket, int N, void *const ten
                 return RAR_EALIGN;
         }
     }
+    // the N ranks' copies of a segment must be distinct memory (each rank
+    // writes its own copy; shared memory would race)
+    Range r[kMaxRanks];
+    for (const Segment &s : b->segs[bucket]) {
+        for (int n = 0; n < N; ++n) {
+            const uintptr_t t = (uintptr_t)tensors[(int64_t)n * b->n_tensors + s.tensor] + (uintptr_t)s.toff * es;
+            r[n] = {t, t + (uintptr_t)s.len * es};
+        }
+        std::sort(r, r + N, [](const Range &a, const Range &c) { return a.lo < c.lo; });
+        for (int n = 1; n < N; ++n)
+            if (r[n].lo < r[n - 1].hi)
+                return RAR_EINVAL;
+    }
     return RAR_OK;
 }
 

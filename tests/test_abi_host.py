@@ -167,3 +167,29 @@ def test_bucket_arena_checks_alignment_and_arguments():
     assert L.rar_bucket_allreduce_arena(b16.handle, 2, 0, 0, api._ptr_array([FAKE, 0]), None, None) == api.EINVAL
     assert L.rar_bucket_allreduce_arena(b16.handle, 0, 0, 0, ar, None, None) == api.EINVAL
     assert L.rar_bucket_allreduce_arena(None, 2, 0, 0, ar, None, None) == api.EINVAL
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    from ring_all_reduce_amd._lib import LIB_PATH
+    exe = tmp_path / "c_abi_check"
+    src = pathlib.Path(__file__).resolve().parent / "c_abi_check.c"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{ROOT / 'include'}",
+                    str(src), str(LIB_PATH), f"-Wl,-rpath,{LIB_PATH.parent}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "c abi ok" in r.stdout
+
+
+def test_bucket_tensors_must_not_overlap_across_ranks():
+    L = lib()
+    b = api.rar_bucket_plan([100, 50], api.F32, 4 * 64)
+    # rank-major pointers: rank 0 (t0, t1), rank 1 (t0, t1); rank 1's tensor 0 is rank 0's tensor 0
+    same = api._ptr_array([FAKE, FAKE + 4096, FAKE, FAKE + 8192])
+    bufs = api._ptr_array([FAKE + (1 << 30), FAKE + (1 << 30) + 4096])
+    assert L.rar_bucket_allreduce_mean(b.handle, 2, 0, 0, same, bufs, None) == api.EINVAL
+    assert L.rar_bucket_pack(b.handle, 0, 2, same, bufs, None) == api.EINVAL
