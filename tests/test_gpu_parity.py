@@ -594,3 +594,28 @@ def test_bucket_tensors_direct_with_misaligned_views(skew, dt):
         got = keep[n][shift:shift + total]
         got = _bits16(got) if dt == api.BF16 else got.cpu().numpy()
         assert got.tobytes() == stream[n].tobytes(), f"rank {n}: first diff {_first_diff(got, stream[n])}"
+
+
+def test_hundred_repeats_with_varied_launch_shapes_are_identical():
+    # race check: 100 runs from the same inputs with workgroup caps drawn at
+    # random (grid-stride loops of every length) must give identical bits
+    N, P = 4, 1_000_003
+    g = _host_f32(N, P, 21)
+    pristine = [torch.from_numpy(x).to(DEV) for x in g]
+    w0 = torch.linspace(-0.05, 0.05, P, device=DEV)
+    ref = [x.copy() for x in g]
+    wr = w0.cpu().numpy().copy()
+    oracle.ring_allreduce_f32(ref, oracle.partition(N, P), wr, 0.1)
+    rng = np.random.default_rng(99)
+    for rep in range(100):
+        algo = api.FUSED if rep % 2 == 0 else api.RING
+        d = [t.clone() for t in pristine]
+        wd = w0.clone()
+        plan = api.rar_plan(N, P)
+        api.rar_plan_set_algo(plan, algo)
+        api.rar_plan_set_grid(plan, int(rng.choice([0, 1, 3, 17, 64, 255, 1024, 5000])))
+        api.rar_allreduce_sgd(plan, d, wd, 0.1, P)
+        torch.cuda.synchronize()
+        for n in (0, N - 1):
+            assert d[n].cpu().numpy().tobytes() == ref[n].tobytes(), f"rep {rep} algo {algo} rank {n}"
+        assert wd.cpu().numpy().tobytes() == wr.tobytes(), f"rep {rep} weights"
