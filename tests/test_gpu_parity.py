@@ -619,3 +619,66 @@ def test_hundred_repeats_with_varied_launch_shapes_are_identical():
         for n in (0, N - 1):
             assert d[n].cpu().numpy().tobytes() == ref[n].tobytes(), f"rep {rep} algo {algo} rank {n}"
         assert wd.cpu().numpy().tobytes() == wr.tobytes(), f"rep {rep} weights"
+
+
+@pytest.mark.parametrize("algo", [api.FUSED, api.RING])
+def test_bf16_special_values(algo):
+    # bf16 infinities, NaN, subnormals and values whose mean rounds to the
+    # largest finite bf16 or overflows to infinity, placed at chunk heads,
+    # tails and bodies.
+    N, P = 4, 8 * 1000 + 5
+    rng = np.random.default_rng(3)
+    g = [oracle.f32_to_bf16(rng.standard_normal(P).astype(np.float32)) for _ in range(N)]
+    off = oracle.partition(N, P, api.BALANCED, 2)
+    specials = [0x7F80, 0xFF80, 0x7FC1, 0x0001, 0x8001, 0x0080, 0x7F7F, 0xFF7F]
+    for c in range(N):
+        for i, s in enumerate(specials):
+            e = int(off[c]) + i * 3
+            g[(c + i) % N][e] = s
+        for r in range(N):
+            g[r][int(off[c]) + 40] = 0x7F7F  # mean of equal maxima: the maximum itself
+            g[r][int(off[c]) + 41] = 0x0001  # smallest subnormal everywhere
+    w0 = np.zeros(P, np.float32)
+    d = _bf16_dev(g)
+    wd = torch.from_numpy(w0.copy()).to(DEV)
+    plan = api.rar_plan(N, P, api.BF16)
+    api.rar_plan_set_algo(plan, algo)
+    api.rar_allreduce_sgd(plan, d, wd, 1e-3, P)
+    torch.cuda.synchronize()
+    ref = [x.copy() for x in g]
+    wr = w0.copy()
+    oracle.ring_allreduce_bf16(ref, off, wr, 1e-3)
+    for n in range(N):
+        got = _bits16(d[n])
+        gf, rf = oracle.bf16_to_f32(got), oracle.bf16_to_f32(ref[n])
+        nan = np.isnan(rf)
+        assert np.array_equal(np.isnan(gf), nan), f"rank {n}: NaN positions differ"
+        assert got[~nan].tobytes() == ref[n][~nan].tobytes(), f"rank {n}: first diff {_first_diff(got, ref[n])}"
+    _assert_bits(wd.cpu().numpy(), wr, "weights")
+
+
+@pytest.mark.parametrize("dt", [api.F32, api.BF16])
+def test_buckets_with_tiny_and_empty_tensors(dt):
+    # empty tensors, one-element tensors and buckets smaller than N elements
+    N = 8
+    numels = [0, 1, 0, 3, 1, 0, 17, 2, 1]
+    es = 4 if dt == api.F32 else 2
+    tdt = torch.float32 if dt == api.F32 else torch.bfloat16
+    rng = np.random.default_rng(8)
+    for bucket_elems in (1, 3, 5, 40):
+        host = [[rng.integers(-9, 9, k).astype(np.float32) for k in numels] for _ in range(N)]
+        tensors = [[torch.from_numpy(x.copy()).to(DEV).to(tdt) for x in rank] for rank in host]
+        b = api.rar_bucket_plan(numels, dt, es * bucket_elems)
+        for algo in (api.FUSED, api.RING):
+            ts = [[t.clone() for t in rank] for rank in tensors]
+            _, mx = api.rar_bucket_count(b)
+            bufs = [torch.empty(max(mx, 1), dtype=tdt, device=DEV) for _ in range(N)]
+            api.rar_bucket_allreduce_mean(b, ts, bufs, api.BALANCED, algo)
+            torch.cuda.synchronize()
+            for t, k in enumerate(numels):
+                S = sum(host[n][t].astype(np.float64) for n in range(N))
+                expect = (S / N).astype(np.float32)  # integer inputs: every order is exact
+                for n in (0, N - 1):
+                    got = ts[n][t].float().cpu().numpy()
+                    want = expect if dt == api.F32 else oracle.bf16_to_f32(oracle.f32_to_bf16(expect))
+                    assert np.array_equal(got, want), (bucket_elems, algo, t, n)
