@@ -40,6 +40,11 @@
  * bf16 plan set to RAR_ALGO_RING (rar_plan_set_algo, or a bucket call that
  * builds such a plan for itself); it lives until the plan is destroyed.
  *
+ * Graph capture: the execute and bucket calls only enqueue kernels and
+ * stream waits (no allocation, synchronisation or memset), so they can be
+ * captured into a HIP graph and replayed, once the plans they use exist and
+ * any bf16 ring workspace has been allocated by rar_plan_set_algo.
+ *
  * Errors: every argument is checked before any device work is enqueued; on
  * error nothing is enqueued and a negative rar_status is returned.
  * RAR_EHIP means a HIP call failed; hipGetLastError() has the detail.

@@ -682,3 +682,59 @@ def test_buckets_with_tiny_and_empty_tensors(dt):
                     got = ts[n][t].float().cpu().numpy()
                     want = expect if dt == api.F32 else oracle.bf16_to_f32(oracle.f32_to_bf16(expect))
                     assert np.array_equal(got, want), (bucket_elems, algo, t, n)
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture: every call enqueues kernels only (no allocation, no
+# synchronisation, no memset), so it can be captured and replayed
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["fused_sgd", "ring_sgd", "bf16_ring_sgd", "bucket_tensors"])
+def test_graph_capture_replays_match_eager(path):
+    N = 8
+    if path == "bucket_tensors":
+        specs = synth.transformer_tensors(1, d=64, h=256, V=900)
+        numels = [s.numel for s in specs]
+        b = api.rar_bucket_plan(numels, api.F32, 4 * 20_000)
+        pristine = [[torch.randn(k, device=DEV) for k in numels] for _ in range(N)]
+        live = [[t.clone() for t in rank] for rank in pristine]
+        run = lambda: api.rar_bucket_allreduce_mean(b, live, None)
+        restore = lambda: [t.copy_(p) for rl, rp in zip(live, pristine) for t, p in zip(rl, rp)]
+        state = lambda: torch.cat([t.reshape(-1) for rank in live for t in rank]).clone()
+    else:
+        P = 1_000_003
+        dt = api.BF16 if path.startswith("bf16") else api.F32
+        tdt = torch.bfloat16 if dt == api.BF16 else torch.float32
+        plan = api.rar_plan(N, P, dt)
+        api.rar_plan_set_algo(plan, api.FUSED if path == "fused_sgd" else api.RING)  # allocates now, not in capture
+        pristine = [torch.randn(P, device=DEV).to(tdt) for _ in range(N)]
+        w0 = torch.linspace(-0.05, 0.05, P, device=DEV)
+        live = [t.clone() for t in pristine]
+        w = w0.clone()
+        run = lambda: api.rar_allreduce_sgd(plan, live, w, 0.01, P)
+        restore = lambda: ([t.copy_(p) for t, p in zip(live, pristine)], w.copy_(w0))
+        state = lambda: torch.cat([t.float() for t in live] + [w]).clone()
+    # eager reference
+    restore()
+    run()
+    torch.cuda.synchronize()
+    eager = state()
+    # capture (after a warm-up on a side stream, as torch requires)
+    restore()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        restore()
+        torch.cuda.synchronize()
+        _ = torch.randn(1000, device=DEV).sum().item()  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        got = state()
+        assert torch.equal(got.view(torch.int32), eager.view(torch.int32)), f"{path}: replay {rep} differs"
