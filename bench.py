@@ -97,7 +97,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-mode", action="store_true",
-                    help="headline kernel and the copy calibration only (for rocprofv3 counter runs)")
+                    help="headline kernel, the ring-step path and the copy calibration only "
+                         "(for rocprofv3 counter runs)")
     ap.add_argument("--grid", type=int, default=0, help="max workgroups per launch (0: library default)")
     args = ap.parse_args()
 
@@ -142,9 +143,15 @@ def main():
 
     if args.profile_mode:
         cal = CopyCalibration(dev)
+        ring = api.rar_plan(N, P, api.F32 if es == 4 else api.BF16, api.BALANCED)
+        api.rar_plan_set_algo(ring, api.RING)
         for _ in range(args.warmup + args.steps):
             step()
             cal.run_once(stream)
+            if sgd:
+                api.rar_allreduce_sgd(ring, bufs, w, wl.lr, P, stream)
+            else:
+                api.rar_allreduce_mean(ring, bufs, P, stream)
         torch.cuda.synchronize()
         print(json.dumps({"profile_mode": True, "workload": wl.name, "launches": args.warmup + args.steps,
                           "copy_bytes_per_launch": cal.bytes, "kernel_src_sha256_16": kernel_sha()}))
@@ -224,6 +231,23 @@ class CopyCalibration:
 # Other rows
 # ---------------------------------------------------------------------------
 
+def time_cold(fn, reps, flush, stream):
+    """Per-call times (ms) of fn, each after writing `flush` (1 GB) on the
+    same stream; the events bracket fn alone."""
+    import torch
+    out = []
+    fn()
+    for _ in range(reps):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
 def secondary_rows(dev, stream, reps=5):
     import torch
     from ring_all_reduce_amd import api, synth
@@ -251,6 +275,39 @@ def secondary_rows(dev, stream, reps=5):
     add("read_1.2GB_torch_sum", cal.bytes // 2, lambda: cal.src.sum())
     add("write_1.2GB_torch_fill_", cal.bytes // 2, lambda: cal.dst.fill_(0.5))
     del cal
+    torch.cuda.empty_cache()
+
+    # small workloads: hot (back to back) and cold (1 GB written before every
+    # call, which evicts L2 and the 256 MB Infinity Cache), as latency
+    flush = torch.empty(250_000_000, dtype=torch.float32, device=dev)
+    for key in (1, 2):
+        wl = synth.WORKLOADS[key]
+        N, P = wl.N, wl.P
+        bufs = synth.rank_gradients(wl, dev)
+        sgd = wl.lr is not None
+        w = synth.weights(wl, dev) if sgd else None
+        nb = alg_bytes(N, P, 4, sgd)
+        kind = "ring_f32"
+        leg = oracle_timer(kind, bufs, w, wl.lr, one_thread=True)
+        for algo, an in ((api.FUSED, "fused"), (api.RING, "ring")):
+            plan = api.rar_plan(N, P)
+            api.rar_plan_set_algo(plan, algo)
+            if sgd:
+                fn = lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream)
+            else:
+                fn = lambda: api.rar_allreduce_mean(plan, bufs, P, stream)
+            hot_total, hot, _ = time_launches(fn, 20, 3, stream)
+            cold = time_cold(fn, 10, flush, stream)
+            r = {"row": f"{wl.name}_{an}_latency", "algo": an,
+                 "hot_us": round(1e3 * sum(hot) / len(hot), 2), "cold_us": round(1e3 * sum(cold) / len(cold), 2),
+                 "hot_alg_GBps": round(nb / (sum(hot) / len(hot) * 1e-3) / 1e9, 1),
+                 "cold_alg_GBps": round(nb / (sum(cold) / len(cold) * 1e-3) / 1e9, 1),
+                 "note": "cold: 1 GB written before each call; hot: back to back (data cache-resident)"}
+            r.update(leg())
+            rows.append(r)
+            log(f"row {r['row']}: {r}")
+        del bufs, w
+    del flush
     torch.cuda.empty_cache()
 
     # workloads 2 and 3 (binary32, SGD): fused, ring steps, reduce-scatter + owner SGD
@@ -397,7 +454,7 @@ def overlap_row(wl, b, infos, arenas, dev, stream, nb, reps=3):
             "producer": "per bucket: bf16 4096^3 matmul + copy of the bucket into every arena"}
 
 
-def oracle_timer(kind, bufs, w, lr, sample_elems=20_000_000, bucket_elems=None):
+def oracle_timer(kind, bufs, w, lr, sample_elems=20_000_000, bucket_elems=None, one_thread=False):
     """Time the CPU oracle once on a prefix of the row's own inputs (copied to
     the host); returns a callable giving the row's oracle fields (computed
     once, shared by the rows of one workload)."""
@@ -435,6 +492,18 @@ def oracle_timer(kind, bufs, w, lr, sample_elems=20_000_000, bucket_elems=None):
         cache.update({"cpu_oracle_GBps": round(nb / dt / 1e9, 3),
                       "cpu_oracle_sample": f"{N} ranks x {P} elements ({kind}), {dt:.2f} s, "
                                            f"{oracle.get_threads()} threads"})
+        if one_thread and kind == "ring_f32":
+            host1 = [t[:P].float().cpu().numpy().copy() for t in bufs]
+            wh1 = w[:P].cpu().numpy().copy() if w is not None else None
+            threads = oracle.get_threads()
+            oracle.set_threads(1)
+            try:
+                t1 = time.perf_counter()
+                oracle.ring_allreduce_f32(host1, oracle.partition(N, P), wh1, lr)
+                d1 = time.perf_counter() - t1
+            finally:
+                oracle.set_threads(threads)
+            cache["cpu_oracle_1thread_GBps"] = round(nb / d1 / 1e9, 3)
         return cache
     return leg
 

@@ -151,7 +151,7 @@ def ring_allreduce_f32(bufs: Sequence[np.ndarray], off: np.ndarray, w: np.ndarra
     sent = np.zeros(N, dtype=np.int64)
     recv = np.zeros(N, dtype=np.int64)
     rc = lib().oracle_ring_f32(N, _ptr(off, _i64p), _as_ptr_array(bufs, _f32p),
-                               _ptr(w, _f32p) if w is not None else None, ctypes.c_float(lr),
+                               _ptr(w, _f32p) if w is not None else None, ctypes.c_float(0.0 if lr is None else lr),
                                _ptr(sent, _i64p), _ptr(recv, _i64p))
     _check(rc, "oracle_ring_f32")
     return sent, recv
@@ -173,7 +173,7 @@ def ring_partial_f32(bufs: Sequence[np.ndarray], off: np.ndarray, sr_steps: int 
     recv = np.zeros(N, dtype=np.int64)
     trace = np.full((2 * N * max(N - 1, 0), 4), -1, dtype=np.int32)
     rc = lib().oracle_ring_f32_ex(N, _ptr(off, _i64p), _as_ptr_array(bufs, _f32p),
-                                  _ptr(w, _f32p) if w is not None else None, ctypes.c_float(lr),
+                                  _ptr(w, _f32p) if w is not None else None, ctypes.c_float(0.0 if lr is None else lr),
                                   _ptr(sent, _i64p), _ptr(recv, _i64p), int(sr_steps),
                                   int(ag_steps), trace.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
     _check(rc, "oracle_ring_f32_ex")
@@ -203,7 +203,7 @@ def ring_allreduce_bf16(bufs: Sequence[np.ndarray], off: np.ndarray, w: np.ndarr
     recv = np.zeros(N, dtype=np.int64)
     ptrs = _as_ptr_array(bufs, _u16p)
     rc = lib().oracle_ring_bf16(N, _ptr(off, _i64p), ptrs, ptrs,
-                                _ptr(w, _f32p) if w is not None else None, ctypes.c_float(lr),
+                                _ptr(w, _f32p) if w is not None else None, ctypes.c_float(0.0 if lr is None else lr),
                                 _ptr(sent, _i64p), _ptr(recv, _i64p))
     _check(rc, "oracle_ring_bf16")
     return sent, recv
@@ -217,7 +217,7 @@ def naive_reduce_f32(bufs: Sequence[np.ndarray], w: np.ndarray | None = None, lr
     sent = np.zeros(N, dtype=np.int64)
     recv = np.zeros(N, dtype=np.int64)
     rc = lib().oracle_naive_f32(N, P, _as_ptr_array(bufs, _f32p),
-                                _ptr(w, _f32p) if w is not None else None, ctypes.c_float(lr),
+                                _ptr(w, _f32p) if w is not None else None, ctypes.c_float(0.0 if lr is None else lr),
                                 _ptr(sent, _i64p), _ptr(recv, _i64p))
     _check(rc, "oracle_naive_f32")
     return sent, recv
