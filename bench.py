@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import statistics
 import os
 import pathlib
 import re
@@ -194,6 +195,8 @@ def main():
             "traffic": committed_traffic(wl.name) if args.algo == "fused" else None,
             "algorithmic_bytes_per_launch": nbytes,
             "avg_launch_ms": round(kern_ms, 5),
+            "median_launch_ms": round(statistics.median(per_ms), 5),
+            "min_launch_ms": round(min(per_ms), 5),
         },
     }
     del bufs, w
@@ -256,7 +259,8 @@ def secondary_rows(dev, stream, reps=5):
     def add(name, nbytes, fn, moved=None, extra=None, oracle_leg=None):
         total, per, _ = time_launches(fn, reps, 2, stream)
         ms = total / reps
-        r = {"row": name, "ms": round(ms, 4), "alg_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        r = {"row": name, "ms": round(ms, 4), "ms_median": round(statistics.median(per), 4),
+             "ms_min": round(min(per), 4), "alg_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
              "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         if moved:
             r["moved_GBps"] = round(moved / (ms * 1e-3) / 1e9, 1)
@@ -300,6 +304,8 @@ def secondary_rows(dev, stream, reps=5):
             cold = time_cold(fn, 10, flush, stream)
             r = {"row": f"{wl.name}_{an}_latency", "algo": an,
                  "hot_us": round(1e3 * sum(hot) / len(hot), 2), "cold_us": round(1e3 * sum(cold) / len(cold), 2),
+                 "hot_us_median": round(1e3 * statistics.median(hot), 2), "hot_us_min": round(1e3 * min(hot), 2),
+                 "cold_us_median": round(1e3 * statistics.median(cold), 2), "cold_us_min": round(1e3 * min(cold), 2),
                  "hot_alg_GBps": round(nb / (sum(hot) / len(hot) * 1e-3) / 1e9, 1),
                  "cold_alg_GBps": round(nb / (sum(cold) / len(cold) * 1e-3) / 1e9, 1),
                  "note": "cold: 1 GB written before each call; hot: back to back (data cache-resident)"}
@@ -383,10 +389,15 @@ def secondary_rows(dev, stream, reps=5):
         if el not in plans:
             plans[el] = api.rar_plan(wl.N, el)
 
-    def arena_step():
+    def arena_per_slice():
         for (so, el, _) in infos:
             api.rar_allreduce_mean(plans[el], [a[so:so + el] for a in arenas], el, stream)
-    add(f"{wl.name}_zero_copy_arena", nb, arena_step, None, {"buckets": nbk}, bucket_leg)
+    # one call: the buckets' chunks batched into shared launches
+    add(f"{wl.name}_zero_copy_arena", nb,
+        lambda: api.rar_bucket_allreduce_arena(b, arenas, None, api.BALANCED, api.FUSED, stream),
+        None, {"buckets": nbk}, bucket_leg)
+    # the same slices, one rar_allreduce_mean call (one launch) per bucket
+    add(f"{wl.name}_zero_copy_arena_per_bucket_calls", nb, arena_per_slice, None, {"buckets": nbk}, bucket_leg)
     del tensors, bucket_bufs
     rows.append(overlap_row(wl, b, infos, arenas, dev, stream, nb))
     log(f"row {rows[-1]['row']}: {rows[-1]}")

@@ -207,6 +207,8 @@ rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void *const buc
  * With RAR_ALGO_FUSED and N in {2, 4, 8, 10, 16, 40} the reduction reads and
  * writes the tensors directly (each bucket segment cut at the bucket's chunk
  * boundaries; 2*N*size bytes moved per bucket) and bucket_bufs may be NULL.
+ * The jobs of consecutive buckets then share launches, so all N*n_tensors
+ * tensors must be pairwise disjoint memory (RAR_EINVAL otherwise).
  * Otherwise each bucket is packed into bucket_bufs[n] (N device buffers of at
  * least max_bucket_elems elements, 16-byte aligned, reused by every bucket),
  * reduced with `algo`, and unpacked. */
@@ -225,7 +227,10 @@ rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunki
  * records the events on its own stream; the waits are enqueued, the call
  * does not block the host.  Every bucket start must be 16-byte aligned
  * (RAR_EALIGN otherwise; a bucket size that is a multiple of 16 bytes gives
- * that).  Results are bit-identical to rar_allreduce_mean on each slice. */
+ * that), and the N arenas (total elements each) must not overlap
+ * (RAR_EINVAL).  With RAR_ALGO_FUSED and N in {2, 4, 8, 10, 16, 40} the
+ * buckets between two ready events share launches.  Results are
+ * bit-identical to rar_allreduce_mean on each slice. */
 rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
                                       void *const arenas[], void *const ready_events[], void *stream);
 

@@ -395,6 +395,8 @@ struct rar_buckets_s {
     rar_dtype dtype = RAR_F32;
     int n_tensors = 0;
     int64_t per_bucket = 0;
+    int64_t total = 0;              // elements of all tensors
+    std::vector<int64_t> numel;     // per tensor
     std::vector<int64_t> start, elems;
     std::vector<std::vector<Segment>> segs;
     int64_t max_elems = 0;
@@ -427,6 +429,8 @@ extern "C" rar_status rar_bucket_plan(int n_tensors, const int64_t numel[], rar_
     b->dtype = dtype;
     b->n_tensors = n_tensors;
     b->per_bucket = B;
+    if (n_tensors > 0)
+        b->numel.assign(numel, numel + n_tensors);
     int64_t stream_pos = 0, fill = 0;
     std::vector<Segment> cur;
     auto close = [&]() {
@@ -451,6 +455,7 @@ extern "C" rar_status rar_bucket_plan(int n_tensors, const int64_t numel[], rar_
     }
     if (fill > 0)
         close();
+    b->total = stream_pos;
     *out = b;
     return RAR_OK;
 }
@@ -541,6 +546,93 @@ rar_status check_bucket_args(rar_buckets_t b, int bucket, int N, void *const ten
     return RAR_OK;
 }
 
+// Byte ranges [lo, hi) must be pairwise disjoint (empty ranges are ignored).
+bool disjoint(std::vector<Range> &r)
+{
+    r.erase(std::remove_if(r.begin(), r.end(), [](const Range &x) { return x.hi <= x.lo; }), r.end());
+    std::sort(r.begin(), r.end(), [](const Range &a, const Range &c) { return a.lo < c.lo; });
+    for (size_t i = 1; i < r.size(); ++i)
+        if (r[i].lo < r[i - 1].hi)
+            return false;
+    return true;
+}
+
+// Every tensor of every rank is distinct memory.  Jobs of consecutive
+// buckets share a launch, so memory that two tensors share would race.
+rar_status check_tensors_disjoint(rar_buckets_t b, int N, void *const tensors[])
+{
+    const int es = elem_bytes(b->dtype);
+    std::vector<Range> r;
+    r.reserve((size_t)N * b->n_tensors);
+    for (int n = 0; n < N; ++n)
+        for (int t = 0; t < b->n_tensors; ++t) {
+            const uintptr_t lo = (uintptr_t)tensors[(int64_t)n * b->n_tensors + t];
+            if (b->numel[t] > 0 && !lo)
+                return RAR_EINVAL;
+            r.push_back({lo, lo + (uintptr_t)b->numel[t] * es});
+        }
+    return disjoint(r) ? RAR_OK : RAR_EINVAL;
+}
+
+// Jobs of the grouped bucket kernel, gathered across buckets and launched
+// min(kMaxJobs, kMaxJobPtrs / N) at a time.  A launch's grid has one row of
+// workgroups per job, as long as its longest job, so jobs under 1 MiB per
+// rank (short tensors, bucket ends) gather in a batch of their own and do not
+// pad their rows to the length of full chunks.  The jobs are disjoint, so the
+// grouping changes no result.
+struct JobBatch {
+    struct Batch {
+        rar::JobsParams jp{};
+        int64_t max_len = 0;
+    };
+    static constexpr int64_t kSmallBytes = 1 << 20;
+    rar_dtype dt;
+    int N;
+    hipStream_t st;
+    int per_launch;
+    Batch big, small;
+
+    JobBatch(rar_dtype dt_, int N_, hipStream_t st_)
+        : dt(dt_), N(N_), st(st_), per_launch(std::min(rar::kMaxJobs, rar::kMaxJobPtrs / N_))
+    {
+    }
+
+    rar_status flush(Batch &bt)
+    {
+        if (bt.jp.njobs == 0)
+            return RAR_OK;
+        hipError_t e = rar::launch_bucket_jobs(dt, N, bt.jp, kDefaultBlocks, bt.max_len, st);
+        bt.jp.njobs = 0;
+        bt.max_len = 0;
+        return hip_status(e);
+    }
+
+    rar_status flush()
+    {
+        rar_status rc = flush(big);
+        return rc != RAR_OK ? rc : flush(small);
+    }
+
+    // One job of `len` elements whose fold starts at rank c; rank n's first
+    // element is at first[n].
+    rar_status add(int64_t len, int c, char *const first[])
+    {
+        if (len <= 0)
+            return RAR_OK;
+        Batch &bt = len * elem_bytes(dt) < kSmallBytes ? small : big;
+        const int j = bt.jp.njobs;
+        bool same_align = true;
+        for (int n = 0; n < N; ++n) {
+            bt.jp.ptr[j * N + n] = first[n];
+            same_align &= (((uintptr_t)first[n] ^ (uintptr_t)first[0]) & 15) == 0;
+        }
+        bt.jp.job[j] = {len, c, same_align ? 1 : 0};
+        bt.jp.njobs = j + 1;
+        bt.max_len = std::max(bt.max_len, len);
+        return bt.jp.njobs == per_launch ? flush(bt) : RAR_OK;
+    }
+};
+
 // pack (to_bucket) or unpack, in launches of at most kMaxCopyJobs segments
 rar_status bucket_copy(rar_buckets_t b, int bucket, int N, void *const tensors[], void *const bucket_bufs[],
                        bool to_bucket, hipStream_t st)
@@ -625,42 +717,25 @@ namespace {
 
 // Bucket k reduced in place in the tensors: each segment is cut at the
 // bucket's chunk boundaries into jobs with a uniform fold start.
-rar_status bucket_direct(rar_buckets_t b, int k, int N, const rar_plan_s *pl, void *const tensors[], hipStream_t st)
+rar_status bucket_direct(rar_buckets_t b, int k, int N, const rar_plan_s *pl, void *const tensors[], JobBatch &jb)
 {
     const int es = elem_bytes(b->dtype);
-    const int per_launch = std::min(rar::kMaxJobs, rar::kMaxJobPtrs / N);
-    rar::JobsParams jp{};
-    int64_t max_len = 0;
-    auto flush = [&]() -> rar_status {
-        hipError_t e = rar::launch_bucket_jobs(b->dtype, N, jp, block_budget(pl), max_len, st);
-        jp.njobs = 0;
-        max_len = 0;
-        return hip_status(e);
-    };
+    char *first[kMaxRanks];
     for (const Segment &sg : b->segs[k]) {
         for (int c = 0; c < N; ++c) {
             const int64_t lo = std::max(sg.boff, pl->ct.off[c]);
             const int64_t hi = std::min(sg.boff + sg.len, pl->ct.off[c + 1]);
             if (hi <= lo)
                 continue;
-            const int j = jp.njobs;
-            bool same_align = true;
-            for (int n = 0; n < N; ++n) {
-                char *t = static_cast<char *>(tensors[(int64_t)n * b->n_tensors + sg.tensor]);
-                jp.ptr[j * N + n] = t + (sg.toff + (lo - sg.boff)) * es;
-                same_align &= (((uintptr_t)jp.ptr[j * N + n] ^ (uintptr_t)jp.ptr[j * N]) & 15) == 0;
-            }
-            jp.job[j] = {hi - lo, c, same_align ? 1 : 0};
-            jp.njobs = j + 1;
-            max_len = std::max(max_len, hi - lo);
-            if (jp.njobs == per_launch) {
-                rar_status rc = flush();
-                if (rc != RAR_OK)
-                    return rc;
-            }
+            for (int n = 0; n < N; ++n)
+                first[n] = static_cast<char *>(tensors[(int64_t)n * b->n_tensors + sg.tensor]) +
+                           (sg.toff + (lo - sg.boff)) * es;
+            rar_status rc = jb.add(hi - lo, c, first);
+            if (rc != RAR_OK)
+                return rc;
         }
     }
-    return jp.njobs ? flush() : RAR_OK;
+    return RAR_OK;
 }
 
 }  // namespace
@@ -683,12 +758,16 @@ extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chun
         return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (direct) {
+        rc = check_tensors_disjoint(b, N, tensors);
+        if (rc != RAR_OK)
+            return rc;
+        JobBatch jb(b->dtype, N, st);
         for (int k = 0; k < nb; ++k) {
-            rc = bucket_direct(b, k, N, plan_of[k], tensors, st);
+            rc = bucket_direct(b, k, N, plan_of[k], tensors, jb);
             if (rc != RAR_OK)
                 return rc;
         }
-        return RAR_OK;
+        return jb.flush();
     }
     for (int k = 0; k < nb; ++k) {
         rc = bucket_copy(b, k, N, tensors, bucket_bufs, true, st);
@@ -718,11 +797,40 @@ extern "C" rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chu
     for (int k = 0; k < nb; ++k)
         if ((b->start[k] * es) & 15)
             return RAR_EALIGN;
+    std::vector<Range> ar;
+    for (int n = 0; n < N; ++n)
+        ar.push_back({(uintptr_t)arenas[n], (uintptr_t)arenas[n] + (uintptr_t)b->total * es});
+    if (!disjoint(ar))
+        return RAR_EINVAL;
     std::vector<rar_plan_t> plan_of;
     rar_status rc = bucket_plans(b, N, chunking, algo, plan_of);
     if (rc != RAR_OK)
         return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N)) {
+        // every chunk of every bucket is one job; the buckets between two
+        // ready events share launches
+        JobBatch jb(b->dtype, N, st);
+        char *first[kMaxRanks];
+        for (int k = 0; k < nb; ++k) {
+            if (ready_events && ready_events[k]) {
+                rc = jb.flush();
+                if (rc != RAR_OK)
+                    return rc;
+                if (hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0) != hipSuccess)
+                    return RAR_EHIP;
+            }
+            const rar_plan_s *pl = plan_of[k];
+            for (int c = 0; c < N; ++c) {
+                for (int n = 0; n < N; ++n)
+                    first[n] = static_cast<char *>(arenas[n]) + (b->start[k] + pl->ct.off[c]) * es;
+                rc = jb.add(pl->ct.off[c + 1] - pl->ct.off[c], c, first);
+                if (rc != RAR_OK)
+                    return rc;
+            }
+        }
+        return jb.flush();
+    }
     void *slice[kMaxRanks];
     for (int k = 0; k < nb; ++k) {
         if (ready_events && ready_events[k] &&

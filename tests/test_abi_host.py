@@ -193,3 +193,29 @@ def test_bucket_tensors_must_not_overlap_across_ranks():
     bufs = api._ptr_array([FAKE + (1 << 30), FAKE + (1 << 30) + 4096])
     assert L.rar_bucket_allreduce_mean(b.handle, 2, 0, 0, same, bufs, None) == api.EINVAL
     assert L.rar_bucket_pack(b.handle, 0, 2, same, bufs, None) == api.EINVAL
+
+
+def test_bucket_tensors_must_not_overlap_across_tensors_or_buckets():
+    """Jobs of consecutive buckets share a launch, so the direct path rejects
+    any two tensors (of any ranks, in any buckets) that share memory."""
+    L = lib()
+    # 64-element buckets: tensor 0 (100) fills bucket 0 and part of bucket 1, tensor 1 (50) the rest
+    b = api.rar_bucket_plan([100, 50], api.F32, 4 * 64)
+    assert api.rar_bucket_count(b)[0] == 3
+    # rank 0's tensor 1 starts inside rank 0's tensor 0 (different buckets)
+    alias = api._ptr_array([FAKE, FAKE + 200, FAKE + 4096, FAKE + 8192])
+    assert L.rar_bucket_allreduce_mean(b.handle, 2, 0, 0, alias, None, None) == api.EINVAL
+    # rank 1's tensor 1 overlaps rank 0's tensor 0's last element
+    alias = api._ptr_array([FAKE, FAKE + 4096, FAKE + 8192, FAKE + 396])
+    assert L.rar_bucket_allreduce_mean(b.handle, 2, 0, 0, alias, None, None) == api.EINVAL
+    # a null pointer for a non-empty tensor
+    alias = api._ptr_array([FAKE, FAKE + 4096, FAKE + 8192, 0])
+    assert L.rar_bucket_allreduce_mean(b.handle, 2, 0, 0, alias, None, None) == api.EINVAL
+
+
+def test_bucket_arenas_must_not_overlap():
+    L = lib()
+    b = api.rar_bucket_plan([100, 50], api.F32, 4 * 64)  # 150 elements = 600 bytes per arena
+    assert L.rar_bucket_allreduce_arena(b.handle, 2, 0, 0, api._ptr_array([FAKE, FAKE + 592]),
+                                        None, None) == api.EINVAL
+    assert L.rar_bucket_allreduce_arena(b.handle, 2, 0, 0, api._ptr_array([FAKE, FAKE]), None, None) == api.EINVAL
