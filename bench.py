@@ -276,7 +276,8 @@ def secondary_rows(dev, stream, reps=5):
     add("copy_1.2GB_rar_copy_kernel", cal.bytes, lambda: cal.run_once(stream))
     add("copy_1.2GB_torch_copy_", cal.bytes, lambda: cal.dst.copy_(cal.src))
     # one-stream read-only and write-only references (torch reductions / fills)
-    add("read_1.2GB_torch_sum", cal.bytes // 2, lambda: cal.src.sum())
+    add("read_1.2GB_torch_sum", cal.bytes // 2, lambda: cal.src.sum(),
+        extra={"note": "torch's own reduction kernel, not a read ceiling"})
     add("write_1.2GB_torch_fill_", cal.bytes // 2, lambda: cal.dst.fill_(0.5))
     del cal
     torch.cuda.empty_cache()
