@@ -32,7 +32,7 @@ struct rar_plan_s {
 
 namespace {
 
-constexpr int kDefaultBlocks = 1 << 24;  // no cap: one tile per workgroup (x is capped at 65535 per job)
+constexpr int kDefaultBlocks = 1 << 24;  // no cap: one tile per workgroup (x is capped at 2^22 - 1 per job)
 
 int elem_bytes(rar_dtype d) { return d == RAR_BF16 ? 2 : 4; }
 

@@ -957,8 +957,10 @@ int blocks_x(int max_blocks, int jobs, int64_t max_vecs, int vpt)
         bx = 1;
     if (bx > need)
         bx = need;
-    if (bx > 65535)
-        bx = 65535;
+    // x may exceed 65535 (only y, the job, may not); a dispatch counts its
+    // work-items in 32 bits, so x times up to 1024 lanes stays below 2^32
+    if (bx > (1 << 22) - 1)
+        bx = (1 << 22) - 1;
     return (int)bx;
 }
 
@@ -1070,7 +1072,7 @@ hipError_t launch_sr_step(rar_dtype dt, const StepParams &p, bool first, bool la
 {
     const dim3 b(kThreads);
     if (dt == RAR_F32) {
-        constexpr int VPT = 2;
+        constexpr int VPT = 1;
         const dim3 g(blocks_x(max_blocks, p.N, max_chunk / 4 + 1, VPT), p.N);
         if (!last)
             hipLaunchKernelGGL((rar_sr_step_f32<VPT, false, false>), g, b, 0, st, p);
@@ -1103,7 +1105,7 @@ hipError_t launch_copy(const CopyParams &p, int max_blocks, int64_t max_job_byte
 {
     if (p.njobs <= 0)
         return hipSuccess;
-    constexpr int VPT = 2;
+    constexpr int VPT = 1;
     const dim3 g(blocks_x(max_blocks, p.njobs, max_job_bytes / 16 + 1, VPT), p.njobs);
     hipLaunchKernelGGL((rar_copy<VPT>), g, dim3(kThreads), 0, st, p);
     return hipGetLastError();
@@ -1111,7 +1113,7 @@ hipError_t launch_copy(const CopyParams &p, int max_blocks, int64_t max_job_byte
 
 hipError_t launch_pair_add(const PairParams &p, bool last, bool sgd, int max_blocks, hipStream_t st)
 {
-    constexpr int VPT = 2;
+    constexpr int VPT = 1;
     const dim3 g(blocks_x(max_blocks, 1, p.P / 4 + 1, VPT), 1);
     const dim3 b(kThreads);
     if (!last)
