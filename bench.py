@@ -120,7 +120,10 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     if wl.layers:
-        raise SystemExit("the headline step is a flat workload; bucketed timing is in rows")
+        if not args.profile_mode:
+            raise SystemExit("the headline step is a flat workload; bucketed timing is in rows")
+        profile_bucketed(wl, dev, stream, args.warmup + args.steps)
+        return
     N, P = wl.N, wl.P
     es = 4 if wl.dtype == "f32" else 2
     sgd = wl.lr is not None
@@ -212,6 +215,29 @@ def main():
 # ---------------------------------------------------------------------------
 # Plain copy calibration (known bytes), also the copy-ceiling row
 # ---------------------------------------------------------------------------
+
+def profile_bucketed(wl, dev, stream, iters):
+    """Counter runs of the bucketed workload: per iteration, the reduction
+    straight from the tensor lists, the 1.2 GB calibration copy, and the
+    reduction over the per-rank arenas (one call each)."""
+    import torch
+    from ring_all_reduce_amd import api, synth
+    specs, ranks = synth.transformer_rank_tensors(wl, dev)
+    tensors = [ts for (_, ts) in ranks]
+    arenas = [flat for (flat, _) in ranks]
+    b = api.rar_bucket_plan([sp.numel for sp in specs], api.F32, wl.bucket_bytes)
+    cal = CopyCalibration(dev)
+    torch.cuda.synchronize()
+    for _ in range(iters):
+        api.rar_bucket_allreduce_mean(b, tensors, None, api.BALANCED, api.FUSED, stream)
+        cal.run_once(stream)
+        api.rar_bucket_allreduce_arena(b, arenas, None, api.BALANCED, api.FUSED, stream)
+    torch.cuda.synchronize()
+    total = sum(sp.numel for sp in specs)
+    print(json.dumps({"profile_mode": True, "workload": wl.name, "calls_per_path": iters,
+                      "algorithmic_bytes_per_call": alg_bytes(wl.N, total, 4, False),
+                      "copy_bytes_per_launch": cal.bytes, "kernel_src_sha256_16": kernel_sha()}))
+
 
 class CopyCalibration:
     """A 1.2 GB device-to-device copy through the library's own dwordx4 copy
