@@ -738,3 +738,64 @@ def test_graph_capture_replays_match_eager(path):
         torch.cuda.synchronize()
         got = state()
         assert torch.equal(got.view(torch.int32), eager.view(torch.int32)), f"{path}: replay {rep} differs"
+
+
+# ---------------------------------------------------------------------------
+# Buckets batched into shared launches: jobs of a full chunk (over 1 MiB per
+# rank) and short ones (small tensors, bucket ends) go to separate batches
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,dt", [(2, api.F32), (4, api.F32), (8, api.F32), (10, api.F32), (16, api.F32),
+                                  (40, api.F32), (4, api.BF16), (10, api.BF16)])
+def test_bucket_batches_mix_big_and_small_jobs(N, dt):
+    es = 4 if dt == api.F32 else 2
+    # chunk length just above the 1 MiB split (40 ranks: all jobs short, 8 per launch)
+    c = (1 << 20) // es + 57_000 if N != 40 else 30_011
+    B = N * c
+    numels = [B + B // 2, 5, 2048, (7 * B) // 10 + 3, 17, B + 11, 1, 3000]
+    total = sum(numels)
+    rng = np.random.default_rng(1000 + N + es)
+    if dt == api.F32:
+        host = [rng.standard_normal(total, dtype=np.float32) * np.float32(1e-3) for _ in range(N)]
+        tdt = torch.float32
+    else:
+        host = [synth.student_t3_bf16(total, 5000 + n, 1e-3, "cpu").view(torch.int16).numpy().view(np.uint16).copy()
+                for n in range(N)]
+        tdt = torch.bfloat16
+    # expected values: each bucket packed and run through the oracle's literal ring
+    layout = oracle.bucket_layout(numels, es, es * B)
+    starts = np.concatenate([[0], np.cumsum(numels)])
+    expect = [h.copy() for h in host]
+    for segs in layout:
+        size = sum(s[3] for s in segs)
+        part = [np.concatenate([host[n][starts[t] + toff:starts[t] + toff + ln] for (t, toff, _, ln) in segs])
+                for n in range(N)]
+        if dt == api.F32:
+            oracle.ring_allreduce_f32(part, oracle.partition(N, size))
+        else:
+            oracle.ring_allreduce_bf16(part, oracle.partition(N, size, oracle.BALANCED, 2))
+        for n in range(N):
+            for (t, toff, boff, ln) in segs:
+                expect[n][starts[t] + toff:starts[t] + toff + ln] = part[n][boff:boff + ln]
+    b = api.rar_bucket_plan(numels, dt, es * B)
+    assert api.rar_bucket_count(b)[0] == len(layout)
+
+    def upload():
+        if dt == api.F32:
+            return [torch.from_numpy(h.copy()).to(DEV) for h in host]
+        return [torch.from_numpy(h.view(np.int16).copy()).to(DEV).view(torch.bfloat16) for h in host]
+
+    for path in ("tensors", "arena"):
+        arenas = upload()
+        if path == "tensors":
+            views = [[a[starts[t]:starts[t + 1]] for t in range(len(numels))] for a in arenas]
+            api.rar_bucket_allreduce_mean(b, views, None, api.BALANCED, api.FUSED)
+        else:
+            api.rar_bucket_allreduce_arena(b, arenas, None, api.BALANCED, api.FUSED)
+        torch.cuda.synchronize()
+        for n in range(N):
+            got = arenas[n].cpu()
+            got = got.numpy() if dt == api.F32 else got.view(torch.int16).numpy().view(np.uint16)
+            assert got.tobytes() == expect[n].tobytes(), \
+                f"{path} rank {n}: first diff {_first_diff(got.view(np.uint32) if dt == api.F32 else got, expect[n].view(np.uint32) if dt == api.F32 else expect[n])}"
+        del arenas
