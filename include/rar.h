@@ -51,6 +51,9 @@
  * Thread safety: a plan is immutable after rar_plan_set_algo; a plan without
  * a workspace may be used from several host threads and streams at once.  A
  * bf16 ring plan owns one workspace and must be used by one stream at a time.
+ * A bucket handle may be used from several threads and streams at once (its
+ * plan cache is locked), except with dtype bf16 and RAR_ALGO_RING, whose
+ * cached plans share one workspace per bucket size: one stream at a time.
  */
 #ifndef RAR_H
 #define RAR_H

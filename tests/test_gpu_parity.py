@@ -799,3 +799,61 @@ def test_bucket_batches_mix_big_and_small_jobs(N, dt):
             assert got.tobytes() == expect[n].tobytes(), \
                 f"{path} rank {n}: first diff {_first_diff(got.view(np.uint32) if dt == api.F32 else got, expect[n].view(np.uint32) if dt == api.F32 else expect[n])}"
         del arenas
+
+
+# ---------------------------------------------------------------------------
+# Several host threads, each on its own stream, share one plan and one bucket
+# handle (ctypes releases the GIL inside the library call)
+# ---------------------------------------------------------------------------
+
+def test_plan_and_buckets_shared_across_threads_and_streams():
+    import threading
+    N, T, ITERS = 8, 4, 6
+    specs = synth.transformer_tensors(1, d=64, h=256, V=500)
+    numels = [s.numel for s in specs]
+    bucket_bytes = 4 * 9_000
+    P = 100_003
+    b = api.rar_bucket_plan(numels, api.F32, bucket_bytes)
+    plan = api.rar_plan(N, P)
+    work = []
+    for th in range(T):
+        rng = np.random.default_rng(700 + th)
+        tens = [[rng.standard_normal(k).astype(np.float32) for k in numels] for _ in range(N)]
+        flat = [rng.standard_normal(P).astype(np.float32) for _ in range(N)]
+        w = rng.uniform(-0.05, 0.05, P).astype(np.float32)
+        exp_t = [[x.copy() for x in rank] for rank in tens]
+        oracle.bucketed_ring_f32(exp_t, bucket_bytes)
+        exp_f = [x.copy() for x in flat]
+        exp_w = w.copy()
+        oracle.ring_allreduce_f32(exp_f, oracle.partition(N, P), exp_w, 0.01)
+        work.append((tens, flat, w, exp_t, exp_f, exp_w))
+    errors = []
+
+    def run(th):
+        try:
+            tens, flat, w, exp_t, exp_f, exp_w = work[th]
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for it in range(ITERS):
+                    dt = [[torch.from_numpy(x).to(DEV, non_blocking=False) for x in rank] for rank in tens]
+                    df = [torch.from_numpy(x).to(DEV) for x in flat]
+                    dw = torch.from_numpy(w).to(DEV)
+                    st.synchronize()
+                    api.rar_bucket_allreduce_mean(b, dt, None, api.BALANCED, api.FUSED, stream=st)
+                    api.rar_allreduce_sgd(plan, df, dw, 0.01, P, stream=st)
+                    st.synchronize()
+                    for n in (0, N - 1):
+                        for t in range(len(numels)):
+                            assert dt[n][t].cpu().numpy().tobytes() == exp_t[n][t].tobytes(), (th, it, n, t)
+                        assert df[n].cpu().numpy().tobytes() == exp_f[n].tobytes(), (th, it, n)
+                    assert dw.cpu().numpy().tobytes() == exp_w.tobytes(), (th, it)
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(th,)) for th in range(T)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
