@@ -519,6 +519,28 @@ def test_bucket_layout_of_the_transformer():
     assert covered == numels
 
 
+def test_bucketed_ring_fold_order_per_bucket():
+    """Every bucket has its own chunk table, so an element's fold starts at
+    the rank of its chunk within its own bucket ([Gibiansky] §Applying
+    allreduce to deep learning: each subset is all-reduced on its own).
+    The triple (2^24, 1, -2^24-2) on ranks 0, 1, 2 gives a different mean for
+    each fold start: from rank 0, fl(2^24+1) = 2^24, then -2, mean -2/3; from
+    rank 1, fl(1-2^24-2) = -2^24, then 0; from rank 2, -2 then -1, mean -1/3."""
+    N = 3
+    numels = [13, 9]  # 22 elements in buckets of 10, 10 and 2
+    by_start = {0: np.float32(-2.0) / np.float32(3.0), 1: np.float32(0.0),
+                2: np.float32(-1.0) / np.float32(3.0)}
+    # chunk of each element, written out: buckets of 10 split 4/3/3, the last (2) split 1/1/0
+    chunk_of = [0, 0, 0, 0, 1, 1, 1, 2, 2, 2] * 2 + [0, 1]
+    vals = [np.float32(2.0 ** 24), np.float32(1.0), np.float32(-(2.0 ** 24) - 2.0)]
+    ranks = [[np.full(k, vals[n], dtype=np.float32) for k in numels] for n in range(N)]
+    oracle.bucketed_ring_f32(ranks, bucket_bytes=4 * 10)
+    want = np.array([by_start[c] for c in chunk_of], dtype=np.float32)
+    for n in range(N):
+        got = np.concatenate(ranks[n])
+        assert got.tobytes() == want.tobytes(), (n, got, want)
+
+
 def test_bucketed_ring_integer_exact():
     N = 3
     specs = synth.transformer_tensors(1, d=8, h=16, V=10)
