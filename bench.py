@@ -377,11 +377,15 @@ def secondary_rows(dev, stream, reps=5):
     w = synth.weights(wl, dev)
     nb = alg_bytes(N, P, 2, True)
     bf_leg = oracle_timer("ring_bf16", bufs, w, wl.lr)
+    # ring steps per element: first scatter-reduce step 2+2 read, 4 written (fp32
+    # workspace); each middle step 2+4 read, 4 written; last 2+4 read, 2 written,
+    # + 8 for w; each all-gather step 2 read, 2 written
+    moved_bf_ring = (8 + (N - 3) * 10 + 16 + (N - 1) * 4) * P
     for algo, an in ((api.FUSED, "fused"), (api.RING, "ring")):
         plan = api.rar_plan(N, P, api.BF16)
         api.rar_plan_set_algo(plan, algo)
-        add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream), None,
-            {"algo": an}, bf_leg)
+        add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream),
+            moved_bf_ring if algo == api.RING else None, {"algo": an}, bf_leg)
         del plan
     del bufs, w
     torch.cuda.empty_cache()
