@@ -8,7 +8,9 @@
 // "The communication problem"; [DDPpage] "[PyTorch] GPU 분산 학습 1 - DP / DDP
 // / FSDP 개념", sections "DDP" and "FSDP".
 #include <algorithm>
+#include <cstdint>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <tuple>
@@ -60,6 +62,20 @@ void cut_chunks(int N, int64_t P, rar_chunking mode, int es, rar::ChunkTable &ct
 int block_budget(const rar_plan_s *pl) { return pl->max_blocks > 0 ? pl->max_blocks : kDefaultBlocks; }
 
 rar_status hip_status(hipError_t e) { return e == hipSuccess ? RAR_OK : RAR_EHIP; }
+
+// No C++ exception crosses the C ABI: the entry points that build host
+// containers run their body through this (allocation failure -> RAR_ENOMEM).
+template <class F>
+rar_status no_throw(F &&body)
+{
+    try {
+        return body();
+    } catch (const std::bad_alloc &) {
+        return RAR_ENOMEM;
+    } catch (...) {
+        return RAR_EINVAL;
+    }
+}
 
 struct Range {
     uintptr_t lo, hi;
@@ -420,44 +436,49 @@ extern "C" rar_status rar_bucket_plan(int n_tensors, const int64_t numel[], rar_
     const int64_t B = bucket_bytes / elem_bytes(dtype);
     if (B <= 0)
         return RAR_EINVAL;
-    for (int t = 0; t < n_tensors; ++t)
-        if (numel[t] < 0)
-            return RAR_EINVAL;
-    rar_buckets_s *b = new (std::nothrow) rar_buckets_s;
-    if (!b)
-        return RAR_ENOMEM;
-    b->dtype = dtype;
-    b->n_tensors = n_tensors;
-    b->per_bucket = B;
-    if (n_tensors > 0)
-        b->numel.assign(numel, numel + n_tensors);
-    int64_t stream_pos = 0, fill = 0;
-    std::vector<Segment> cur;
-    auto close = [&]() {
-        b->start.push_back(stream_pos - fill);
-        b->elems.push_back(fill);
-        b->max_elems = std::max(b->max_elems, fill);
-        b->segs.push_back(std::move(cur));
-        cur.clear();
-        fill = 0;
-    };
+    int64_t total = 0;
     for (int t = 0; t < n_tensors; ++t) {
-        int64_t done = 0;
-        while (done < numel[t]) {
-            const int64_t take = std::min(numel[t] - done, B - fill);
-            cur.push_back({t, done, fill, take});
-            done += take;
-            fill += take;
-            stream_pos += take;
-            if (fill == B)
-                close();
-        }
+        if (numel[t] < 0 || numel[t] > INT64_MAX - total)
+            return RAR_EINVAL;
+        total += numel[t];
     }
-    if (fill > 0)
-        close();
-    b->total = stream_pos;
-    *out = b;
-    return RAR_OK;
+    if (total / B >= INT32_MAX)  // bucket indices are int
+        return RAR_EINVAL;
+    return no_throw([&]() -> rar_status {
+        std::unique_ptr<rar_buckets_s> b(new rar_buckets_s);
+        b->dtype = dtype;
+        b->n_tensors = n_tensors;
+        b->per_bucket = B;
+        if (n_tensors > 0)
+            b->numel.assign(numel, numel + n_tensors);
+        int64_t stream_pos = 0, fill = 0;
+        std::vector<Segment> cur;
+        auto close = [&]() {
+            b->start.push_back(stream_pos - fill);
+            b->elems.push_back(fill);
+            b->max_elems = std::max(b->max_elems, fill);
+            b->segs.push_back(std::move(cur));
+            cur.clear();
+            fill = 0;
+        };
+        for (int t = 0; t < n_tensors; ++t) {
+            int64_t done = 0;
+            while (done < numel[t]) {
+                const int64_t take = std::min(numel[t] - done, B - fill);
+                cur.push_back({t, done, fill, take});
+                done += take;
+                fill += take;
+                stream_pos += take;
+                if (fill == B)
+                    close();
+            }
+        }
+        if (fill > 0)
+            close();
+        b->total = stream_pos;
+        *out = b.release();
+        return RAR_OK;
+    });
 }
 
 extern "C" rar_status rar_bucket_destroy(rar_buckets_t b)
@@ -544,6 +565,13 @@ rar_status check_bucket_args(rar_buckets_t b, int bucket, int N, void *const ten
                 return RAR_EINVAL;
     }
     return RAR_OK;
+}
+
+bool valid_bucket_call(int N, rar_chunking chunking, rar_algo algo)
+{
+    return N >= 1 && N <= kMaxRanks &&
+           (chunking == RAR_CHUNK_BALANCED || chunking == RAR_CHUNK_CEIL || chunking == RAR_CHUNK_ALIGN16) &&
+           (algo == RAR_ALGO_FUSED || algo == RAR_ALGO_RING || algo == RAR_ALGO_NAIVE);
 }
 
 // Byte ranges [lo, hi) must be pairwise disjoint (empty ranges are ignored).
@@ -743,106 +771,110 @@ rar_status bucket_direct(rar_buckets_t b, int k, int N, const rar_plan_s *pl, vo
 extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
                                                 void *const tensors[], void *const bucket_bufs[], void *stream)
 {
-    if (!b)
-        return RAR_EINVAL;
-    const int nb = (int)b->segs.size();
-    const bool direct = algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N);
-    for (int k = 0; k < nb; ++k) {
-        rar_status rc = check_bucket_args(b, k, N, tensors, bucket_bufs, !direct);
-        if (rc != RAR_OK)
-            return rc;
-    }
-    std::vector<rar_plan_t> plan_of;
-    rar_status rc = bucket_plans(b, N, chunking, algo, plan_of);
-    if (rc != RAR_OK)
-        return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (direct) {
-        rc = check_tensors_disjoint(b, N, tensors);
-        if (rc != RAR_OK)
-            return rc;
-        JobBatch jb(b->dtype, N, st);
+    return no_throw([&]() -> rar_status {
+        if (!b || !valid_bucket_call(N, chunking, algo))
+            return RAR_EINVAL;
+        const int nb = (int)b->segs.size();
+        const bool direct = algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N);
         for (int k = 0; k < nb; ++k) {
-            rc = bucket_direct(b, k, N, plan_of[k], tensors, jb);
+            rar_status rc = check_bucket_args(b, k, N, tensors, bucket_bufs, !direct);
             if (rc != RAR_OK)
                 return rc;
         }
-        return jb.flush();
-    }
-    for (int k = 0; k < nb; ++k) {
-        rc = bucket_copy(b, k, N, tensors, bucket_bufs, true, st);
-        if (rc == RAR_OK)
-            rc = rar_allreduce_mean(plan_of[k], bucket_bufs, b->elems[k], stream);
-        if (rc == RAR_OK)
-            rc = bucket_copy(b, k, N, tensors, bucket_bufs, false, st);
+        std::vector<rar_plan_t> plan_of;
+        rar_status rc = bucket_plans(b, N, chunking, algo, plan_of);
         if (rc != RAR_OK)
             return rc;
-    }
-    return RAR_OK;
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        if (direct) {
+            rc = check_tensors_disjoint(b, N, tensors);
+            if (rc != RAR_OK)
+                return rc;
+            JobBatch jb(b->dtype, N, st);
+            for (int k = 0; k < nb; ++k) {
+                rc = bucket_direct(b, k, N, plan_of[k], tensors, jb);
+                if (rc != RAR_OK)
+                    return rc;
+            }
+            return jb.flush();
+        }
+        for (int k = 0; k < nb; ++k) {
+            rc = bucket_copy(b, k, N, tensors, bucket_bufs, true, st);
+            if (rc == RAR_OK)
+                rc = rar_allreduce_mean(plan_of[k], bucket_bufs, b->elems[k], stream);
+            if (rc == RAR_OK)
+                rc = bucket_copy(b, k, N, tensors, bucket_bufs, false, st);
+            if (rc != RAR_OK)
+                return rc;
+        }
+        return RAR_OK;
+    });
 }
 
 extern "C" rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
                                                  void *const arenas[], void *const ready_events[], void *stream)
 {
-    if (!b || !arenas || N < 1 || N > kMaxRanks)
-        return RAR_EINVAL;
-    const int es = elem_bytes(b->dtype);
-    const int nb = (int)b->segs.size();
-    for (int n = 0; n < N; ++n) {
-        if (!arenas[n])
+    return no_throw([&]() -> rar_status {
+        if (!b || !arenas || !valid_bucket_call(N, chunking, algo))
             return RAR_EINVAL;
-        if ((uintptr_t)arenas[n] & 15)
-            return RAR_EALIGN;
-    }
-    for (int k = 0; k < nb; ++k)
-        if ((b->start[k] * es) & 15)
-            return RAR_EALIGN;
-    std::vector<Range> ar;
-    for (int n = 0; n < N; ++n)
-        ar.push_back({(uintptr_t)arenas[n], (uintptr_t)arenas[n] + (uintptr_t)b->total * es});
-    if (!disjoint(ar))
-        return RAR_EINVAL;
-    std::vector<rar_plan_t> plan_of;
-    rar_status rc = bucket_plans(b, N, chunking, algo, plan_of);
-    if (rc != RAR_OK)
-        return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N)) {
-        // every chunk of every bucket is one job; the buckets between two
-        // ready events share launches
-        JobBatch jb(b->dtype, N, st);
-        char *first[kMaxRanks];
-        for (int k = 0; k < nb; ++k) {
-            if (ready_events && ready_events[k]) {
-                rc = jb.flush();
-                if (rc != RAR_OK)
-                    return rc;
-                if (hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0) != hipSuccess)
-                    return RAR_EHIP;
-            }
-            const rar_plan_s *pl = plan_of[k];
-            for (int c = 0; c < N; ++c) {
-                for (int n = 0; n < N; ++n)
-                    first[n] = static_cast<char *>(arenas[n]) + (b->start[k] + pl->ct.off[c]) * es;
-                rc = jb.add(pl->ct.off[c + 1] - pl->ct.off[c], c, first);
-                if (rc != RAR_OK)
-                    return rc;
-            }
+        const int es = elem_bytes(b->dtype);
+        const int nb = (int)b->segs.size();
+        for (int n = 0; n < N; ++n) {
+            if (!arenas[n])
+                return RAR_EINVAL;
+            if ((uintptr_t)arenas[n] & 15)
+                return RAR_EALIGN;
         }
-        return jb.flush();
-    }
-    void *slice[kMaxRanks];
-    for (int k = 0; k < nb; ++k) {
-        if (ready_events && ready_events[k] &&
-            hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0) != hipSuccess)
-            return RAR_EHIP;
+        for (int k = 0; k < nb; ++k)
+            if ((b->start[k] * es) & 15)
+                return RAR_EALIGN;
+        std::vector<Range> ar;
         for (int n = 0; n < N; ++n)
-            slice[n] = static_cast<char *>(arenas[n]) + b->start[k] * es;
-        rc = rar_allreduce_mean(plan_of[k], slice, b->elems[k], stream);
+            ar.push_back({(uintptr_t)arenas[n], (uintptr_t)arenas[n] + (uintptr_t)b->total * es});
+        if (!disjoint(ar))
+            return RAR_EINVAL;
+        std::vector<rar_plan_t> plan_of;
+        rar_status rc = bucket_plans(b, N, chunking, algo, plan_of);
         if (rc != RAR_OK)
             return rc;
-    }
-    return RAR_OK;
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        if (algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N)) {
+            // every chunk of every bucket is one job; the buckets between two
+            // ready events share launches
+            JobBatch jb(b->dtype, N, st);
+            char *first[kMaxRanks];
+            for (int k = 0; k < nb; ++k) {
+                if (ready_events && ready_events[k]) {
+                    rc = jb.flush();
+                    if (rc != RAR_OK)
+                        return rc;
+                    if (hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0) != hipSuccess)
+                        return RAR_EHIP;
+                }
+                const rar_plan_s *pl = plan_of[k];
+                for (int c = 0; c < N; ++c) {
+                    for (int n = 0; n < N; ++n)
+                        first[n] = static_cast<char *>(arenas[n]) + (b->start[k] + pl->ct.off[c]) * es;
+                    rc = jb.add(pl->ct.off[c + 1] - pl->ct.off[c], c, first);
+                    if (rc != RAR_OK)
+                        return rc;
+                }
+            }
+            return jb.flush();
+        }
+        void *slice[kMaxRanks];
+        for (int k = 0; k < nb; ++k) {
+            if (ready_events && ready_events[k] &&
+                hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0) != hipSuccess)
+                return RAR_EHIP;
+            for (int n = 0; n < N; ++n)
+                slice[n] = static_cast<char *>(arenas[n]) + b->start[k] * es;
+            rc = rar_allreduce_mean(plan_of[k], slice, b->elems[k], stream);
+            if (rc != RAR_OK)
+                return rc;
+        }
+        return RAR_OK;
+    });
 }
 
 // =============================================================================

@@ -219,3 +219,26 @@ def test_bucket_arenas_must_not_overlap():
     assert L.rar_bucket_allreduce_arena(b.handle, 2, 0, 0, api._ptr_array([FAKE, FAKE + 592]),
                                         None, None) == api.EINVAL
     assert L.rar_bucket_allreduce_arena(b.handle, 2, 0, 0, api._ptr_array([FAKE, FAKE]), None, None) == api.EINVAL
+
+
+def test_bucket_plan_rejects_layouts_beyond_int_indices():
+    L = lib()
+    out = ctypes.c_void_p()
+    # 2^40 one-element buckets: more than an int can index
+    arr = (ctypes.c_int64 * 1)(1 << 40)
+    assert L.rar_bucket_plan(1, arr, api.F32, 4, ctypes.byref(out)) == api.EINVAL
+    # element counts whose sum overflows int64
+    arr = (ctypes.c_int64 * 2)((1 << 63) - 1, 1)
+    assert L.rar_bucket_plan(2, arr, api.F32, 1 << 30, ctypes.byref(out)) == api.EINVAL
+
+
+def test_bucket_calls_validate_arguments_even_without_buckets():
+    L = lib()
+    b = api.rar_bucket_plan([], api.F32)
+    assert api.rar_bucket_count(b)[0] == 0
+    empty = api._ptr_array([])
+    for N, chunking, algo in ((0, 0, 0), (65, 0, 0), (2, 7, 0), (2, 0, 9)):
+        assert L.rar_bucket_allreduce_mean(b.handle, N, chunking, algo, empty, None, None) == api.EINVAL
+        assert L.rar_bucket_allreduce_arena(b.handle, N, chunking, algo, api._ptr_array([FAKE] * max(N, 1)),
+                                            None, None) == api.EINVAL
+    assert L.rar_bucket_allreduce_mean(b.handle, 2, 0, 0, empty, None, None) == api.OK
