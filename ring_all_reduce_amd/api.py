@@ -63,6 +63,13 @@ def _ptr_array(xs: Sequence) -> ctypes.Array:
     return arr
 
 
+def _ranks(xs: Sequence, N: int, what: str) -> ctypes.Array:
+    # the library reads exactly N pointers from the array
+    if len(xs) != N:
+        raise ValueError(f"{what}: {len(xs)} entries for {N} ranks")
+    return _ptr_array(xs)
+
+
 def _stream(s) -> int:
     if s is None:
         try:
@@ -135,18 +142,19 @@ def rar_plan_traffic(plan: Plan, rank: int):
 # ---------------------------------------------------------------------------
 
 def rar_allreduce_mean(plan: Plan, bufs: Sequence, P: int, stream=None) -> None:
-    _check(lib().rar_allreduce_mean(plan.handle, _ptr_array(bufs), int(P), _stream(stream)),
+    _check(lib().rar_allreduce_mean(plan.handle, _ranks(bufs, plan.N, "bufs"), int(P), _stream(stream)),
            "rar_allreduce_mean")
 
 
 def rar_allreduce_sgd(plan: Plan, bufs: Sequence, w, lr: float, P: int, stream=None) -> None:
-    _check(lib().rar_allreduce_sgd(plan.handle, _ptr_array(bufs), _addr(w), ctypes.c_float(lr), int(P),
+    _check(lib().rar_allreduce_sgd(plan.handle, _ranks(bufs, plan.N, "bufs"), _addr(w), ctypes.c_float(lr), int(P),
                                    _stream(stream)), "rar_allreduce_sgd")
 
 
 def rar_reduce_scatter_sgd_allgather(plan: Plan, bufs: Sequence, w_reps: Sequence, lr: float, P: int,
                                      stream=None) -> None:
-    _check(lib().rar_reduce_scatter_sgd_allgather(plan.handle, _ptr_array(bufs), _ptr_array(w_reps),
+    _check(lib().rar_reduce_scatter_sgd_allgather(plan.handle, _ranks(bufs, plan.N, "bufs"),
+                                                  _ranks(w_reps, plan.N, "w_reps"),
                                                   ctypes.c_float(lr), int(P), _stream(stream)),
            "rar_reduce_scatter_sgd_allgather")
 
@@ -201,30 +209,36 @@ def rar_bucket_segment(b: Buckets, bucket: int, seg: int):
     return t.value, to.value, bo.value, ln.value
 
 
-def _rank_major(tensors: Sequence[Sequence]) -> ctypes.Array:
+def _rank_major(b: "Buckets", tensors: Sequence[Sequence]) -> ctypes.Array:
+    # the library reads N * n_tensors pointers: every rank must list them all
+    for n, rank in enumerate(tensors):
+        if len(rank) != b.n_tensors:
+            raise ValueError(f"rank {n} lists {len(rank)} tensors; the bucket plan has {b.n_tensors}")
     flat = [x for rank in tensors for x in rank]
     return _ptr_array(flat)
 
 
 def rar_bucket_pack(b: Buckets, bucket: int, tensors: Sequence[Sequence], bucket_bufs: Sequence,
                     stream=None) -> None:
-    _check(lib().rar_bucket_pack(b.handle, int(bucket), len(tensors), _rank_major(tensors),
-                                 _ptr_array(bucket_bufs), _stream(stream)), "rar_bucket_pack")
+    _check(lib().rar_bucket_pack(b.handle, int(bucket), len(tensors), _rank_major(b, tensors),
+                                 _ranks(bucket_bufs, len(tensors), "bucket_bufs"), _stream(stream)),
+           "rar_bucket_pack")
 
 
 def rar_bucket_unpack(b: Buckets, bucket: int, bucket_bufs: Sequence, tensors: Sequence[Sequence],
                       stream=None) -> None:
-    _check(lib().rar_bucket_unpack(b.handle, int(bucket), len(tensors), _ptr_array(bucket_bufs),
-                                   _rank_major(tensors), _stream(stream)), "rar_bucket_unpack")
+    _check(lib().rar_bucket_unpack(b.handle, int(bucket), len(tensors),
+                                   _ranks(bucket_bufs, len(tensors), "bucket_bufs"),
+                                   _rank_major(b, tensors), _stream(stream)), "rar_bucket_unpack")
 
 
 def rar_bucket_allreduce_mean(b: Buckets, tensors: Sequence[Sequence], bucket_bufs=None,
                               chunking: int = BALANCED, algo: int = FUSED, stream=None) -> None:
     """bucket_bufs: N buffers of max_bucket_elems, or None when the reduction
     runs straight from the tensors (RAR_ALGO_FUSED at a supported rank count)."""
-    bufs = None if bucket_bufs is None else _ptr_array(bucket_bufs)
+    bufs = None if bucket_bufs is None else _ranks(bucket_bufs, len(tensors), "bucket_bufs")
     _check(lib().rar_bucket_allreduce_mean(b.handle, len(tensors), int(chunking), int(algo),
-                                           _rank_major(tensors), bufs, _stream(stream)),
+                                           _rank_major(b, tensors), bufs, _stream(stream)),
            "rar_bucket_allreduce_mean")
 
 
@@ -234,6 +248,9 @@ def rar_bucket_allreduce_arena(b: Buckets, arenas: Sequence, ready_events=None, 
     integer hipEvent_t, or None (no wait)."""
     ev = None
     if ready_events is not None:
+        nb = rar_bucket_count(b)[0]
+        if len(ready_events) != nb:
+            raise ValueError(f"{len(ready_events)} ready events for {nb} buckets")
         ev = (ctypes.c_void_p * max(len(ready_events), 1))()
         for i, e in enumerate(ready_events):
             ev[i] = None if e is None else (e if isinstance(e, int) else int(e.cuda_event)) or None

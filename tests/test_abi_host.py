@@ -242,3 +242,25 @@ def test_bucket_calls_validate_arguments_even_without_buckets():
         assert L.rar_bucket_allreduce_arena(b.handle, N, chunking, algo, api._ptr_array([FAKE] * max(N, 1)),
                                             None, None) == api.EINVAL
     assert L.rar_bucket_allreduce_mean(b.handle, 2, 0, 0, empty, None, None) == api.OK
+
+
+def test_binding_rejects_ragged_tensor_lists_and_short_event_lists():
+    b = api.rar_bucket_plan([10, 20], api.F32, 4 * 16)
+    ragged = [[FAKE, FAKE + 4096], [FAKE + 8192]]
+    with pytest.raises(ValueError):
+        api.rar_bucket_allreduce_mean(b, ragged)
+    with pytest.raises(ValueError):
+        api.rar_bucket_pack(b, 0, ragged, [FAKE + (1 << 30), FAKE + (1 << 31)])
+    with pytest.raises(ValueError):
+        api.rar_bucket_allreduce_arena(b, [FAKE, FAKE + (1 << 20)], ready_events=[None])
+
+
+def test_binding_rejects_pointer_lists_of_the_wrong_length():
+    plan = api.rar_plan(4, 100)
+    for bad in ([FAKE] * 3, [FAKE] * 5):
+        with pytest.raises(ValueError):
+            api.rar_allreduce_mean(plan, bad, 100)
+        with pytest.raises(ValueError):
+            api.rar_allreduce_sgd(plan, bad, FAKE + (1 << 30), 0.1, 100)
+    with pytest.raises(ValueError):
+        api.rar_reduce_scatter_sgd_allgather(plan, [FAKE + (i << 20) for i in range(4)], [FAKE + (1 << 30)], 0.1, 100)
