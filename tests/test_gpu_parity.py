@@ -256,25 +256,36 @@ def test_bucket_pack_unpack_roundtrip_unaligned(dt):
         assert torch.equal(arenas[n], backup[n])
 
 
-def test_bucketed_small_transformer_bit_exact():
-    N = 4
+@pytest.mark.parametrize("mode", [api.BALANCED, api.CEIL, api.ALIGN16])
+@pytest.mark.parametrize("N", [4, 10])
+def test_bucketed_small_transformer_bit_exact(N, mode):
+    # buckets of 40,004 elements (16-byte multiples, so arena slices stay
+    # aligned); at N = 10 the three chunkings cut them differently:
+    # balanced 4001 x 4 + 4000 x 6, ceil 4001 x 9 + 3995, align16 4004 x 9 + 3968
     specs = synth.transformer_tensors(2, d=64, h=256, V=1000)
     numels = [s.numel for s in specs]
-    bucket_bytes = 4 * 40_000
+    bucket_bytes = 4 * 40_004
     host = [[np.random.default_rng(100 * n + t).standard_normal(s.numel).astype(np.float32) * 1e-3
              for t, s in enumerate(specs)] for n in range(N)]
-    for algo in (api.FUSED, api.RING):
-        tensors = [[torch.from_numpy(x.copy()).to(DEV) for x in rank] for rank in host]
-        b = api.rar_bucket_plan(numels, api.F32, bucket_bytes)
-        _, mx = api.rar_bucket_count(b)
-        bufs = [torch.empty(mx, device=DEV) for _ in range(N)]
-        api.rar_bucket_allreduce_mean(b, tensors, bufs, api.BALANCED, algo)
+    ref = [[x.copy() for x in rank] for rank in host]
+    oracle.bucketed_ring_f32(ref, bucket_bytes, mode)
+    b = api.rar_bucket_plan(numels, api.F32, bucket_bytes)
+    _, mx = api.rar_bucket_count(b)
+    starts = np.concatenate([[0], np.cumsum(numels)])
+    for path in ("tensors", "arena", "ring"):
+        arenas = [torch.from_numpy(np.concatenate(rank)).to(DEV) for rank in host]
+        tensors = [[a[starts[t]:starts[t + 1]] for t in range(len(numels))] for a in arenas]
+        if path == "tensors":
+            api.rar_bucket_allreduce_mean(b, tensors, None, mode, api.FUSED)
+        elif path == "arena":
+            api.rar_bucket_allreduce_arena(b, arenas, None, mode, api.FUSED)
+        else:
+            bufs = [torch.empty(mx, device=DEV) for _ in range(N)]
+            api.rar_bucket_allreduce_mean(b, tensors, bufs, mode, api.RING)
         torch.cuda.synchronize()
-        ref = [[x.copy() for x in rank] for rank in host]
-        oracle.bucketed_ring_f32(ref, bucket_bytes)
         for n in range(N):
             for t in range(len(specs)):
-                _assert_bits(tensors[n][t].cpu().numpy(), ref[n][t], f"algo {algo} rank {n} tensor {t}")
+                _assert_bits(tensors[n][t].cpu().numpy(), ref[n][t], f"{path} rank {n} tensor {t}")
 
 
 # ---------------------------------------------------------------------------
@@ -657,9 +668,11 @@ def test_bf16_special_values(algo):
     _assert_bits(wd.cpu().numpy(), wr, "weights")
 
 
+@pytest.mark.parametrize("mode", [api.BALANCED, api.CEIL, api.ALIGN16])
 @pytest.mark.parametrize("dt", [api.F32, api.BF16])
-def test_buckets_with_tiny_and_empty_tensors(dt):
+def test_buckets_with_tiny_and_empty_tensors(dt, mode):
     # empty tensors, one-element tensors and buckets smaller than N elements
+    # (CEIL and ALIGN16 leave the last chunks of such buckets empty)
     N = 8
     numels = [0, 1, 0, 3, 1, 0, 17, 2, 1]
     es = 4 if dt == api.F32 else 2
@@ -673,7 +686,7 @@ def test_buckets_with_tiny_and_empty_tensors(dt):
             ts = [[t.clone() for t in rank] for rank in tensors]
             _, mx = api.rar_bucket_count(b)
             bufs = [torch.empty(max(mx, 1), dtype=tdt, device=DEV) for _ in range(N)]
-            api.rar_bucket_allreduce_mean(b, ts, bufs, api.BALANCED, algo)
+            api.rar_bucket_allreduce_mean(b, ts, bufs, mode, algo)
             torch.cuda.synchronize()
             for t, k in enumerate(numels):
                 S = sum(host[n][t].astype(np.float64) for n in range(N))
