@@ -572,6 +572,11 @@ __device__ __forceinline__ void grouped_span_bf16(Base base, float *w, float lr,
                     for (int j = 0; j < PER; ++j) {
                         if (j < cnt) {
                             f32x4 a, b;
+                            // Emits nothing.  Without it the compiler widens each
+                            // x[j] once for all G-1 unrolled hops and keeps the
+                            // 2*PER binary32 vectors live instead of PER packed
+                            // ones: past 128 VGPRs at N = 40, G = 4 (spills).
+                            asm volatile("" : "+v"(x[j]));
                             widen8(x[j], a, b);
                             lo = lo + a;
                             hi = hi + b;
@@ -971,7 +976,7 @@ int blocks_x(int max_blocks, int jobs, int64_t max_vecs, int vpt)
 // per lane and a 32-byte partial sum to pass, gains from two groups at
 // 4-16 ranks and loses from any split at 40.
 constexpr int groups_f32(int N) { return N <= 3 ? 1 : N <= 4 ? 2 : N <= 12 ? 4 : N <= 16 ? 3 : 4; }
-constexpr int groups_bf16(int N) { return N <= 3 ? 1 : N <= 16 ? 2 : 1; }
+constexpr int groups_bf16(int N) { return N <= 3 ? 1 : N <= 16 ? 2 : 4; }
 
 template <int NT>
 hipError_t fused_grouped(rar_dtype dt, const FusedParams &p, int max_blocks, int64_t max_chunk,

@@ -759,7 +759,7 @@ def test_graph_capture_replays_match_eager(path):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("N,dt", [(2, api.F32), (4, api.F32), (8, api.F32), (10, api.F32), (16, api.F32),
-                                  (40, api.F32), (4, api.BF16), (10, api.BF16)])
+                                  (40, api.F32), (4, api.BF16), (10, api.BF16), (40, api.BF16)])
 def test_bucket_batches_mix_big_and_small_jobs(N, dt):
     es = 4 if dt == api.F32 else 2
     # chunk length just above the 1 MiB split (40 ranks: all jobs short, 8 per launch)
