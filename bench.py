@@ -577,7 +577,7 @@ def cpu_baseline(wl, dev, sample_P=100_000_000, min_s=10.0, max_s=30.0):
             "sample": f"{N} ranks x {P} fp32 elements per rank drawn with the workload's seeds and "
                       f"distribution (the full workload has {wl.P}), literal ring with SGD, {runs} runs, "
                       f"{per:.3f} s per run, {t_sum:.1f} s in all",
-            "cpu": _cpu_model()}
+            "cpu": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 def _cpu_model():
