@@ -8,6 +8,8 @@ sampled elements (every chunk boundary +-9 and 10^6 random ones) through the
 oracle's literal ring restricted to those elements, plus whole-array
 properties (all ranks identical).
 """
+import pathlib
+
 import numpy as np
 import pytest
 import torch
@@ -870,3 +872,16 @@ def test_plan_and_buckets_shared_across_threads_and_streams():
         t.join(timeout=120)
     assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
     assert not errors, errors
+
+
+# ---------------------------------------------------------------------------
+# The C ABI from a plain C program (built by __graft_entry__.build())
+# ---------------------------------------------------------------------------
+
+def test_c_program_runs_the_abi_on_the_gpu():
+    import subprocess
+    exe = pathlib.Path(__file__).resolve().parent / "c_gpu_example.bin"
+    assert exe.exists(), "tests/c_gpu_example.bin is not built: run __graft_entry__.build()"
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "bit-exact" in r.stdout
