@@ -94,8 +94,9 @@ __device__ __forceinline__ u32x4 narrow8(f32x4 a, f32x4 b)
 // Span driver
 // ---------------------------------------------------------------------------
 
-// Walk elements [e0, e1) of one job: scalar head and tail on block 0, then the
-// aligned body in tiles (grid-stride over blockIdx.x).  VEC = elements per
+// Walk elements [e0, e1) of one job: scalar head (up to the first index on a
+// 128-byte line) and tail (after the last whole 16-byte group) on block 0,
+// then the body in tiles (grid-stride over blockIdx.x).  VEC = elements per
 // 16 bytes.  elem(e) handles one element; tile(FULL, a0, v0, nvec) handles
 // vectors v0 .. v0+kThreads*VPT-1 of the body that starts at element a0
 // (lane-contiguous), bounds-checked against nvec unless FULL.
@@ -104,18 +105,23 @@ __device__ __forceinline__ void run_span(int64_t e0, int64_t e1, ElemF &&elem, T
 {
     if (e1 <= e0)
         return;
-    int64_t a0 = (e0 + VEC - 1) / VEC * VEC;
-    int64_t a1 = e1 / VEC * VEC;
-    if (a0 > a1) {  // the whole span sits inside one 16-byte group
-        a0 = e1;
-        a1 = e1;
-    }
+    // the body starts at an element index that is a multiple of one 128-byte
+    // line (buffers are allocations, so index and address alignment agree),
+    // so no line is shared by two workgroups' tiles
+    constexpr int64_t LINE = 8 * VEC;
+    int64_t h = (LINE - e0 % LINE) % LINE;
+    if (h > e1 - e0)
+        h = e1 - e0;
+    const int64_t a0 = e0 + h;
+    const int64_t a1 = a0 + (e1 - a0) / VEC * VEC;
     if (blockIdx.x == 0) {
         const int t = threadIdx.x;
-        if (t < a0 - e0)
-            elem(e0 + t);
-        else if (t >= VEC && t < VEC + (e1 - a1))
-            elem(a1 + (t - VEC));
+        if (t < LINE) {
+            if (t < h)
+                elem(e0 + t);
+        } else if (t - LINE < e1 - a1) {
+            elem(a1 + (t - LINE));
+        }
     }
     const int64_t nvec = (a1 - a0) / VEC;
     constexpr int64_t TV = (int64_t)kThreads * VPT;
@@ -404,28 +410,35 @@ __device__ __forceinline__ void span_elem(Base base, float *w, float lr, int c, 
     }
 }
 
-// Head and tail of a span: the elements before the first 16-byte aligned
-// address of base(0) (every rank's base shares that alignment) and after the
-// last whole 16-byte group.  Block bx == 0, lanes < 2*VEC.  Returns the head
-// length h and the number of whole vectors nvec.
+// Head and tail of a span: the elements before the first 128-byte aligned
+// address of base(0) and after the last whole 16-byte group, on block
+// bx == 0, lanes < 128/sizeof(T) (head) and the next VEC lanes (tail).
+// Returns the head length h and the number of whole vectors nvec.
 template <typename T, int NT, bool SGD, class Base>
 __device__ __forceinline__ void span_head_tail(Base base, float *w, float lr, int c, int64_t len, int64_t bx,
                                                int64_t &h, int64_t &nvec)
 {
     constexpr int VEC = 16 / sizeof(T);
+    constexpr int LINE = 128 / sizeof(T);  // elements per 128-byte cache line
     const uintptr_t addr = reinterpret_cast<uintptr_t>(base(0));
-    h = (int64_t)(((16 - (addr & 15)) & 15) / sizeof(T));
+    // The body starts on a cache line of rank 0, so each workgroup's tile
+    // covers whole lines and no line is fetched by two workgroups (a chunk
+    // of 2.5M bf16 elements starts 64 bytes into a line).  The other ranks
+    // share rank 0's offset modulo 16 (modulo 128 for separate allocations).
+    h = (int64_t)(((128 - (addr & 127)) & 127) / sizeof(T));
     if (h > len)
         h = len;
     nvec = (len - h) / VEC;
     const int64_t tail0 = h + nvec * VEC;
-    if (bx != 0 || threadIdx.x >= 2 * VEC)
+    if (bx != 0 || threadIdx.x >= LINE + VEC)
         return;
     const int64_t t = threadIdx.x;
-    if (t < h)
-        span_elem<T, NT, SGD>(base, w, lr, c, t);
-    else if (t >= VEC && t - VEC < len - tail0)
-        span_elem<T, NT, SGD>(base, w, lr, c, tail0 + (t - VEC));
+    if (t < LINE) {
+        if (t < h)
+            span_elem<T, NT, SGD>(base, w, lr, c, t);
+    } else if (t - LINE < len - tail0) {
+        span_elem<T, NT, SGD>(base, w, lr, c, tail0 + (t - LINE));
+    }
 }
 
 // The grouped body over one binary32 span of `len` elements whose fold starts
@@ -847,18 +860,20 @@ __global__ __launch_bounds__(kThreads) void rar_copy(CopyParams p)
         return;
     if ((((uintptr_t)s ^ (uintptr_t)d) & 15) == 0) {
         // same offset within a 16-byte group: scalar units up to the first
-        // aligned group, dwordx4 body, scalar units after the last group
-        const int64_t head = (int64_t)((16 - ((uintptr_t)d & 15)) & 15) < n
-                                 ? (int64_t)((16 - ((uintptr_t)d & 15)) & 15)
-                                 : n;
+        // 128-byte line of d (so no line of d is written by two workgroups),
+        // dwordx4 body, scalar units after the last 16-byte group
+        const int64_t to_line = (int64_t)((128 - ((uintptr_t)d & 127)) & 127);
+        const int64_t head = to_line < n ? to_line : n;
         const int64_t body = (n - head) / 16;
         const int64_t tail0 = head + body * 16;
         if (blockIdx.x == 0) {
-            const int64_t t = threadIdx.x;
-            if (t * unit < head)
-                copy_unit(t * unit);
-            else if (t >= 16 && (t - 16) * unit < n - tail0)
-                copy_unit(tail0 + (t - 16) * unit);
+            const int64_t t = threadIdx.x;  // lanes 0..63: head units; 64..71: tail units
+            if (t < 64) {
+                if (t * unit < head)
+                    copy_unit(t * unit);
+            } else if (t < 72 && (t - 64) * unit < n - tail0) {
+                copy_unit(tail0 + (t - 64) * unit);
+            }
         }
         const u32x4 *s4 = reinterpret_cast<const u32x4 *>(s + head);
         u32x4 *d4 = reinterpret_cast<u32x4 *>(d + head);
