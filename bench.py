@@ -43,7 +43,13 @@ def log(*a):
 
 
 def kernel_sha() -> str:
-    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace removed, so
+    an edit to a comment keeps the recorded counters valid and any change to
+    the code does not."""
+    text = KERNEL_SRC.read_text()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
 
 
 def alg_bytes(N, P, es, sgd):

@@ -15,14 +15,16 @@
 //
 // Work decomposition, shared by every kernel: blockIdx.y selects a job (a
 // chunk of the chunk table, or a copy segment); blockIdx.x and a grid-stride
-// loop walk that job's element range.  The 16-byte aligned body of the range
-// is processed in tiles of kThreads*VPT vectors, lane-contiguous so that one
-// wave instruction touches 1 KiB of consecutive memory; the at most VEC-1
-// elements before the first aligned group (the head) and after the last (the
-// tail) go through a scalar path on block 0's first lanes.  Chunk boundaries
-// need not be 16-byte aligned (a balanced cut of P = 1,000,003 over 4 ranks
-// puts them at 250,001 and 500,002), so the per-chunk span keeps a dwordx4
-// access from ever straddling two chunks whose sums start at different ranks.
+// loop walk that job's element range.  The body of the range starts on a
+// 128-byte cache line and is processed in tiles of kThreads*VPT 16-byte
+// vectors, lane-contiguous so that one wave instruction touches 1 KiB of
+// consecutive memory and each tile covers whole lines (no line is fetched or
+// written by two workgroups).  The elements before that first line (the head)
+// and the at most VEC-1 after the last whole vector (the tail) go through a
+// scalar path on block 0's first lanes.  Chunk boundaries need not be aligned
+// at all (a balanced cut of P = 1,000,003 over 4 ranks puts them at 250,001
+// and 500,002), so the per-chunk span keeps a dwordx4 access from ever
+// straddling two chunks whose sums start at different ranks.
 //
 // Numerics, identical in every kernel: binary32 adds in ring order starting at
 // the chunk's own rank, one IEEE division by N, SGD as w - (lr*m) with both
