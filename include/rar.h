@@ -47,7 +47,9 @@
  *
  * Errors: every argument is checked before any device work is enqueued; on
  * error nothing is enqueued and a negative rar_status is returned.
- * RAR_EHIP means a HIP call failed; hipGetLastError() has the detail.
+ * RAR_EHIP means a HIP launch or runtime call failed, RAR_ENOMEM that a
+ * device allocation did.  The library clears HIP's last-error state when it
+ * returns either, so the caller's next HIP call does not report it again.
  * Thread safety: a plan is immutable after rar_plan_set_algo; a plan without
  * a workspace may be used from several host threads and streams at once.  A
  * bf16 ring plan owns one workspace and must be used by one stream at a time.

@@ -63,6 +63,15 @@ int block_budget(const rar_plan_s *pl) { return pl->max_blocks > 0 ? pl->max_blo
 
 rar_status hip_status(hipError_t e) { return e == hipSuccess ? RAR_OK : RAR_EHIP; }
 
+// A failed HIP runtime call also sets HIP's per-thread "last error", which
+// the caller's next HIP call (a torch kernel launch, say) would report as its
+// own.  The library maps the failure to a status and clears it.
+rar_status hip_failed(hipError_t e)
+{
+    (void)hipGetLastError();
+    return e == hipErrorOutOfMemory ? RAR_ENOMEM : RAR_EHIP;
+}
+
 // No C++ exception crosses the C ABI: the entry points that build host
 // containers run their body through this (allocation failure -> RAR_ENOMEM).
 template <class F>
@@ -271,8 +280,11 @@ extern "C" rar_status rar_plan_destroy(rar_plan_t plan)
     if (!plan)
         return RAR_OK;
     rar_status rc = RAR_OK;
-    if (plan->ws && hipFree(plan->ws) != hipSuccess)
-        rc = RAR_EHIP;
+    if (plan->ws) {
+        const hipError_t e = hipFree(plan->ws);
+        if (e != hipSuccess)
+            rc = hip_failed(e);
+    }
     delete plan;
     return rc;
 }
@@ -288,10 +300,8 @@ extern "C" rar_status rar_plan_set_algo(rar_plan_t plan, rar_algo algo)
     if (algo == RAR_ALGO_RING && plan->dtype == RAR_BF16 && !plan->ws && plan->P > 0 && plan->N > 1) {
         void *p = nullptr;
         const hipError_t e = hipMalloc(&p, (size_t)plan->P * sizeof(float));
-        if (e == hipErrorOutOfMemory)
-            return RAR_ENOMEM;
         if (e != hipSuccess)
-            return RAR_EHIP;
+            return hip_failed(e);
         plan->ws = static_cast<float *>(p);
     }
     plan->algo = algo;
@@ -848,8 +858,9 @@ extern "C" rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chu
                     rc = jb.flush();
                     if (rc != RAR_OK)
                         return rc;
-                    if (hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0) != hipSuccess)
-                        return RAR_EHIP;
+                    const hipError_t e = hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0);
+                    if (e != hipSuccess)
+                        return hip_failed(e);
                 }
                 const rar_plan_s *pl = plan_of[k];
                 for (int c = 0; c < N; ++c) {
@@ -864,9 +875,11 @@ extern "C" rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chu
         }
         void *slice[kMaxRanks];
         for (int k = 0; k < nb; ++k) {
-            if (ready_events && ready_events[k] &&
-                hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0) != hipSuccess)
-                return RAR_EHIP;
+            if (ready_events && ready_events[k]) {
+                const hipError_t e = hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0);
+                if (e != hipSuccess)
+                    return hip_failed(e);
+            }
             for (int n = 0; n < N; ++n)
                 slice[n] = static_cast<char *>(arenas[n]) + b->start[k] * es;
             rc = rar_allreduce_mean(plan_of[k], slice, b->elems[k], stream);
@@ -887,7 +900,7 @@ extern "C" const char *rar_strerror(rar_status s)
     case RAR_EMISMATCH: return "element count differs from the plan";
     case RAR_EALIGN: return "device pointer not 16-byte aligned";
     case RAR_ENOMEM: return "out of memory";
-    case RAR_EHIP: return "HIP runtime error (see hipGetLastError)";
+    case RAR_EHIP: return "HIP runtime error";
     }
     return "unknown status";
 }

@@ -885,3 +885,19 @@ def test_c_program_runs_the_abi_on_the_gpu():
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "bit-exact" in r.stdout
+
+
+# ---------------------------------------------------------------------------
+# Allocation failure is reported, not raised or crashed: a bf16 ring plan
+# whose fp32 workspace cannot exist (2^40 floats = 4 TiB)
+# ---------------------------------------------------------------------------
+
+def test_workspace_allocation_failure_reports_enomem():
+    plan = api.rar_plan(2, 1 << 40, api.BF16)
+    with pytest.raises(api.RarError) as err:
+        api.rar_plan_set_algo(plan, api.RING)
+    assert err.value.status == api.ENOMEM
+    # the plan is still usable with the algorithm it had, and the device is fine
+    api.rar_plan_set_algo(plan, api.FUSED)
+    x = torch.ones(1024, device=DEV)
+    assert float(x.sum()) == 1024.0
