@@ -264,3 +264,45 @@ def test_binding_rejects_pointer_lists_of_the_wrong_length():
             api.rar_allreduce_sgd(plan, bad, FAKE + (1 << 30), 0.1, 100)
     with pytest.raises(ValueError):
         api.rar_reduce_scatter_sgd_allgather(plan, [FAKE + (i << 20) for i in range(4)], [FAKE + (1 << 30)], 0.1, 100)
+
+
+# ---------------------------------------------------------------------------
+# Property tests of the host tables against the oracle over random shapes
+# ---------------------------------------------------------------------------
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=300, deadline=None)
+@given(N=st.integers(1, 64), P=st.integers(0, 10 ** 7), mode=st.sampled_from([api.BALANCED, api.CEIL, api.ALIGN16]),
+       dt=st.sampled_from([api.F32, api.BF16]))
+def test_chunk_table_owner_and_traffic_match_the_oracle(N, P, mode, dt):
+    es = 4 if dt == api.F32 else 2
+    plan = api.rar_plan(N, P, dt, mode)
+    off = oracle.partition(N, P, mode, es)
+    sent_o, recv_o = oracle.ring_traffic(N, off)
+    for c in range(N):
+        o, ln, own = api.rar_plan_chunk(plan, c)
+        assert (o, ln) == (int(off[c]), int(off[c + 1] - off[c]))
+        assert own == oracle.owner(c, N)
+    for n in range(N):
+        assert api.rar_plan_traffic(plan, n) == (int(sent_o[n]), int(recv_o[n]))
+
+
+@settings(max_examples=200, deadline=None)
+@given(numels=st.lists(st.integers(0, 5000), min_size=0, max_size=40),
+       bucket_elems=st.integers(1, 3000), dt=st.sampled_from([api.F32, api.BF16]))
+def test_bucket_layout_matches_the_oracle_on_random_lists(numels, bucket_elems, dt):
+    es = 4 if dt == api.F32 else 2
+    b = api.rar_bucket_plan(numels, dt, es * bucket_elems)
+    layout = oracle.bucket_layout(numels, es, es * bucket_elems)
+    nb, mx = api.rar_bucket_count(b)
+    assert nb == len(layout)
+    assert mx == max((sum(sg[3] for sg in segs) for segs in layout), default=0)
+    start = 0
+    for k, segs in enumerate(layout):
+        so, el, ns = api.rar_bucket_info(b, k)
+        assert (so, el, ns) == (start, sum(sg[3] for sg in segs), len(segs))
+        for j, sg in enumerate(segs):
+            assert api.rar_bucket_segment(b, k, j) == tuple(int(x) for x in sg)
+        start += el
