@@ -901,3 +901,63 @@ def test_workspace_allocation_failure_reports_enomem():
     api.rar_plan_set_algo(plan, api.FUSED)
     x = torch.ones(1024, device=DEV)
     assert float(x.sum()) == 1024.0
+
+
+# ---------------------------------------------------------------------------
+# A seeded random sweep over shapes: rank counts with and without a
+# compile-time kernel, ragged lengths, every chunking, both dtypes, every
+# algorithm, mean and SGD, against the oracle bit for bit
+# ---------------------------------------------------------------------------
+
+def _random_cases(count=48, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        N = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 10, 13, 16, 17, 31, 40, 63, 64]))
+        P = int(rng.integers(0, max(2, 3_000_000 // N)))
+        if i % 5 == 0:
+            P = int(rng.integers(0, 4 * N + 40))  # chunks of a few elements, empty ones
+        dt = api.F32 if i % 3 else api.BF16
+        mode = int(rng.integers(0, 3))
+        algo = int(rng.integers(0, 3 if dt == api.F32 else 2))
+        sgd = bool(rng.integers(0, 2))
+        cases.append((N, P, dt, mode, algo, sgd))
+    return cases
+
+
+@pytest.mark.parametrize("N,P,dt,mode,algo,sgd", _random_cases())
+def test_random_shapes_bit_exact(N, P, dt, mode, algo, sgd):
+    lr = 0.05
+    es = 4 if dt == api.F32 else 2
+    if dt == api.F32:
+        g = _host_f32(N, P, 31 * N + P % 1009)
+        d = _to_dev(g)
+    else:
+        g = _host_bf16(N, P, 17 * N + P % 1009)
+        d = _bf16_dev(g)
+    w0 = np.random.default_rng(P % 7919).uniform(-0.05, 0.05, P).astype(np.float32)
+    wd = torch.from_numpy(w0.copy()).to(DEV)
+    plan = api.rar_plan(N, P, dt, mode)
+    api.rar_plan_set_algo(plan, algo)
+    if sgd:
+        api.rar_allreduce_sgd(plan, d, wd, lr, P)
+    else:
+        api.rar_allreduce_mean(plan, d, P)
+    torch.cuda.synchronize()
+    ref = [x.copy() for x in g]
+    wr = w0.copy()
+    off = oracle.partition(N, P, mode, es)
+    if dt == api.F32 and algo == api.NAIVE:
+        oracle.naive_reduce_f32(ref, wr if sgd else None, lr)
+    elif dt == api.F32:
+        oracle.ring_allreduce_f32(ref, off, wr if sgd else None, lr)
+    else:
+        oracle.ring_allreduce_bf16(ref, off, wr if sgd else None, lr)
+    for n in range(N):
+        got = d[n].cpu().numpy() if dt == api.F32 else _bits16(d[n])
+        if dt == api.F32:
+            _assert_bits(got, ref[n], f"rank {n}")
+        else:
+            assert got.tobytes() == ref[n].tobytes(), f"rank {n}: first diff {_first_diff(got, ref[n])}"
+    if sgd:
+        _assert_bits(wd.cpu().numpy(), wr, "weights")
