@@ -13,10 +13,18 @@ Prints ONE JSON line.  `value` is GB/s of algorithmic bytes (each rank buffer
 read once and written once, w read once and written once: 2*N*P*s + 8*P) per
 second of the timed region.  `roofline` gives the dominant kernel's achieved
 bandwidth from HIP events recorded on the stream the library launches on, against
-MI355X's 8 TB/s HBM3E peak; `traffic` comes from committed rocprofv3 counter
-runs when they were taken on the current kernel source.  `cpu_baseline` is the
-CPU oracle timed on a bounded sample of the same workload.  `rows` measures
-the other paths (ring steps, bf16, buckets, prior-art reducer, plain copy).
+MI355X's 8 TB/s HBM3E peak (average, median and minimum launch time); `traffic`
+comes from committed rocprofv3 counter runs when they were taken on the current
+kernel code.  `cpu_baseline` is the CPU oracle timed on a bounded sample of the
+same workload.  `rows` measures the other paths: ring steps, the single reducer,
+reduce-scatter + owner SGD + weight all-gather, bf16, the bucketed Transformer
+(from the tensor lists, as arena slices, packed for the ring, and overlapped
+with a simulated backward pass), the small workloads as hot and cold latency,
+and plain copy / fill references.
+
+--profile-mode [--workload 3|4|5] runs only the launches the rocprofv3 counter
+passes need (the workload's reduction, the ring steps, a 1.2 GB calibration
+copy of known size) and prints what it ran.
 """
 from __future__ import annotations
 
