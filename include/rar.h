@@ -43,7 +43,11 @@
  * Graph capture: the execute and bucket calls only enqueue kernels and
  * stream waits (no allocation, synchronisation or memset), so they can be
  * captured into a HIP graph and replayed, once the plans they use exist and
- * any bf16 ring workspace has been allocated by rar_plan_set_algo.
+ * any bf16 ring workspace has been allocated by rar_plan_set_algo.  Bucket
+ * calls make their per-size plans on first use (a bf16 RAR_ALGO_RING bucket
+ * call allocates the workspaces then): make one call before capturing.  The
+ * ready events of a captured rar_bucket_allreduce_arena must be recorded
+ * inside the same capture (on a stream forked from the capturing one).
  *
  * Errors: every argument is checked before any device work is enqueued; on
  * error nothing is enqueued and a negative rar_status is returned.
