@@ -961,3 +961,64 @@ def test_random_shapes_bit_exact(N, P, dt, mode, algo, sgd):
             assert got.tobytes() == ref[n].tobytes(), f"rank {n}: first diff {_first_diff(got, ref[n])}"
     if sgd:
         _assert_bits(wd.cpu().numpy(), wr, "weights")
+
+
+def test_graph_capture_arena_with_ready_events():
+    """The overlap path captured whole: a producer stream forked from the
+    capturing stream copies each bucket into the arenas and records the
+    bucket's ready event; the reduction waits for them (one
+    rar_bucket_allreduce_arena call).  Arenas start as NaN before every
+    replay, so reducing a bucket before its copy would show."""
+    N = 4
+    specs = synth.transformer_tensors(1, d=64, h=256, V=900)
+    numels = [s.numel for s in specs]
+    total = sum(numels)
+    b = api.rar_bucket_plan(numels, api.F32, 4 * 20_000)
+    nb, _ = api.rar_bucket_count(b)
+    infos = [api.rar_bucket_info(b, k) for k in range(nb)]
+    pristine = [torch.randn(total, device=DEV) for _ in range(N)]
+    arenas = [torch.empty(total, device=DEV) for _ in range(N)]
+    events = [torch.cuda.Event() for _ in range(nb)]
+
+    def step(main):
+        prod = torch.cuda.Stream()
+        prod.wait_stream(main)  # fork
+        with torch.cuda.stream(prod):
+            for k, (so, el, _) in enumerate(infos):
+                for n in range(N):
+                    arenas[n][so:so + el].copy_(pristine[n][so:so + el])
+                events[k].record(prod)
+        api.rar_bucket_allreduce_arena(b, arenas, events, stream=main)
+        main.wait_stream(prod)  # join
+
+    def poison():
+        for a in arenas:
+            a.fill_(float("nan"))
+
+    poison()
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager = torch.cat(arenas).clone()
+    ref = [p.cpu().numpy().copy() for p in pristine]
+    for k, (so, el, _) in enumerate(infos):
+        part = [np.ascontiguousarray(r[so:so + el]) for r in ref]
+        oracle.ring_allreduce_f32(part, oracle.partition(N, el))
+        for n in range(N):
+            ref[n][so:so + el] = part[n]
+    _assert_bits(eager.cpu().numpy(), np.concatenate(ref), "eager")
+    # warm-up on a side stream, then capture
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    for rep in range(4):
+        poison()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.cat(arenas).view(torch.int32), eager.view(torch.int32)), f"replay {rep} differs"
