@@ -80,6 +80,18 @@ __device__ __forceinline__ uint32_t bf16_rne(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 widen4(u32x2 u)
+{
+    return f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+}
+
+__device__ __forceinline__ u32x2 narrow4(f32x4 a)
+{
+    return u32x2{bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16)};
+}
+
 __device__ __forceinline__ void widen8(u32x4 u, f32x4 &a, f32x4 &b)
 {
     a = f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
@@ -798,41 +810,46 @@ __global__ __launch_bounds__(kThreads) void rar_sr_step_bf16(StepParams p)
         }
     };
 
+    // The tile's 256 vectors (2048 elements) as 512 half-vectors of 4
+    // elements: lane l takes half-vectors 2*v0 + l and 2*v0 + 256 + l.  Each
+    // bf16 access is then 8 bytes and each binary32 access 16 bytes, both
+    // contiguous across a wave, so no binary32 store instruction leaves
+    // gaps (two interleaved 16-byte stores per lane measured 11% slower).
     auto tile = [&](auto full, int64_t a0, int64_t v0, int64_t nvec) {
         constexpr bool FULL = decltype(full)::value;
-        int64_t vi[VPT];
-        bool ok[VPT];
-        lane_vectors<VPT, FULL>(v0, nvec, vi, ok);
-        if (!ok[0])
-            return;
-        const int64_t v = vi[0];
-        u32x4 *d16 = reinterpret_cast<u32x4 *>(dp + a0);
+        const int64_t nh = 2 * nvec;
+        const int64_t h[2] = {2 * v0 + threadIdx.x, 2 * v0 + kThreads + threadIdx.x};
+        const bool ok[2] = {FULL || h[0] < nh, FULL || h[1] < nh};
+        u32x2 *d8 = reinterpret_cast<u32x2 *>(dp + a0);
+        const u32x2 *s8 = reinterpret_cast<const u32x2 *>(sp + a0);
         f32x4 *w4 = reinterpret_cast<f32x4 *>(ws + a0);
-        f32x4 olo, ohi, ilo, ihi;
-        widen8(ld(d16 + v), olo, ohi);
-        if (FIRST) {
-            widen8(ld(reinterpret_cast<const u32x4 *>(sp + a0) + v), ilo, ihi);
-        } else {
-            ilo = ld(w4 + 2 * v);
-            ihi = ld(w4 + 2 * v + 1);
+        f32x4 *wp = SGD ? reinterpret_cast<f32x4 *>(w + a0) : nullptr;
+        f32x4 o[2], in[2], wv[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (!ok[k])
+                continue;
+            o[k] = widen4(ld(d8 + h[k]));
+            in[k] = FIRST ? widen4(ld(s8 + h[k])) : ld(w4 + h[k]);
+            if (LAST && SGD)
+                wv[k] = ld(wp + h[k]);
         }
-        f32x4 slo = olo + ilo, shi = ohi + ihi;
-        if (LAST) {
-            slo = slo / (float)N;
-            shi = shi / (float)N;
-            st(d16 + v, narrow8(slo, shi));
-            if (SGD) {
-                f32x4 *wp = reinterpret_cast<f32x4 *>(w + a0);
-                f32x4 w0 = ld(wp + 2 * v), w1 = ld(wp + 2 * v + 1);
-                const f32x4 s0 = p.lr * slo, s1 = p.lr * shi;
-                w0 = w0 - s0;
-                w1 = w1 - s1;
-                st(wp + 2 * v, w0);
-                st(wp + 2 * v + 1, w1);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (!ok[k])
+                continue;
+            f32x4 sum = o[k] + in[k];
+            if (LAST) {
+                sum = sum / (float)N;
+                st(d8 + h[k], narrow4(sum));
+                if (SGD) {
+                    const f32x4 step = p.lr * sum;
+                    wv[k] = wv[k] - step;
+                    st(wp + h[k], wv[k]);
+                }
+            } else {
+                st(w4 + h[k], sum);
             }
-        } else {
-            st(w4 + 2 * v, slo);
-            st(w4 + 2 * v + 1, shi);
         }
     };
 
