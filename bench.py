@@ -200,6 +200,7 @@ def main():
                    "lr": wl.lr, "chunking": "balanced", "algo": args.algo,
                    "algorithmic_bytes_per_step": nbytes},
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "device": _device_info(props),
         "params_per_s": round(P / (ms_per_step * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
@@ -592,6 +593,22 @@ def cpu_baseline(wl, dev, sample_P=100_000_000, min_s=10.0, max_s=30.0):
                       f"distribution (the full workload has {wl.P}), literal ring with SGD, {runs} runs, "
                       f"{per:.3f} s per run, {t_sum:.1f} s in all",
             "cpu": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def _device_info(props):
+    """Partition modes and memory-clock levels from sysfs (readable without
+    touching the GPU), to tell boxes apart when their numbers differ."""
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count}
+    for key, fname in (("compute_partition", "current_compute_partition"),
+                       ("memory_partition", "current_memory_partition"), ("mclk_levels", "pp_dpm_mclk")):
+        for card in sorted(pathlib.Path("/sys/class/drm").glob("card[0-9]*")):
+            f = card / "device" / fname
+            try:
+                info[key] = " ".join(f.read_text().split())
+                break
+            except OSError:
+                continue
+    return info
 
 
 def _cpu_model():
