@@ -20,9 +20,9 @@
  *      three readings are offered (see oracle_partition).
  *   2. Scatter-reduce, N-1 steps.  At step s rank n sends chunk (n-s) mod N
  *      to rank n+1, which adds the received values into its own copy of that
- *      chunk ([Gibiansky] §Scatter-reduce, the rule "start by sending chunk n
- *      and receiving chunk n-1, then pass on what you received" and its
- *      step-1 table for five GPUs).  Every message is copied out of the
+ *      chunk ([Gibiansky] §Scatter-reduce: rank n first sends chunk n and
+ *      receives chunk n-1, and afterwards forwards what it last received;
+ *      see also its step-1 table for five GPUs).  Every message is copied out of the
  *      sender ("snapshot") before any receiver writes, which is what a send
  *      followed by a receive means.
  *   3. The mean: after step 2 rank n holds the complete sum of chunk
