@@ -143,7 +143,9 @@ def main():
     sgd = wl.lr is not None
     log(f"workload {wl.name}: N={N} P={P} dtype={wl.dtype} sgd={sgd} algo={args.algo}")
 
-    bufs = synth.rank_gradients(wl, dev)
+    # the N logical ranks in one allocation at the library's recommended stride
+    stride = api.rar_rank_stride(P, api.F32 if es == 4 else api.BF16)
+    bufs = synth.rank_gradients_in_pool(wl, stride, dev)
     w = synth.weights(wl, dev) if sgd else None
     plan = api.rar_plan(N, P, api.F32 if es == 4 else api.BF16, api.BALANCED)
     api.rar_plan_set_algo(plan, api.FUSED if args.algo == "fused" else api.RING)
@@ -198,7 +200,8 @@ def main():
         "data": "synthetic (seeded normal gradients, uniform weights, resident in HBM)",
         "config": {"workload": wl.name, "ranks": N, "elems_per_rank": P, "op": "mean+sgd" if sgd else "mean",
                    "lr": wl.lr, "chunking": "balanced", "algo": args.algo,
-                   "algorithmic_bytes_per_step": nbytes},
+                   "algorithmic_bytes_per_step": nbytes,
+                   "rank_layout": f"one allocation, rank n at n * {stride} bytes (rar_rank_stride)"},
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "device": _device_info(props),
         "params_per_s": round(P / (ms_per_step * 1e-3), 1),
@@ -329,7 +332,7 @@ def secondary_rows(dev, stream, reps=5):
     for key in (1, 2):
         wl = synth.WORKLOADS[key]
         N, P = wl.N, wl.P
-        bufs = synth.rank_gradients(wl, dev)
+        bufs = synth.rank_gradients_in_pool(wl, api.rar_rank_stride(P, api.F32), dev)
         sgd = wl.lr is not None
         w = synth.weights(wl, dev) if sgd else None
         nb = alg_bytes(N, P, 4, sgd)
@@ -363,7 +366,7 @@ def secondary_rows(dev, stream, reps=5):
     for key in (2, 3):
         wl = synth.WORKLOADS[key]
         N, P = wl.N, wl.P
-        bufs = synth.rank_gradients(wl, dev)
+        bufs = synth.rank_gradients_in_pool(wl, api.rar_rank_stride(P, api.F32), dev)
         w = synth.weights(wl, dev)
         nb = alg_bytes(N, P, 4, True)
         ring_leg = oracle_timer("ring_f32", bufs, w, wl.lr)
@@ -382,13 +385,21 @@ def secondary_rows(dev, stream, reps=5):
                 lambda: api.rar_reduce_scatter_sgd_allgather(plan, bufs, wreps, wl.lr, P, stream), moved,
                 {"algo": "rs_sgd_ag"}, ring_leg)
             del wreps
+            # the same call on separately allocated rank buffers (torch puts them a
+            # multiple of 4 MiB apart), for the layout's share of the difference
+            sep = synth.rank_gradients(wl, dev)
+            plan = api.rar_plan(N, P)
+            add(f"{wl.name}_fused_separate_allocations", nb,
+                lambda: api.rar_allreduce_sgd(plan, sep, w, wl.lr, P, stream), None,
+                {"algo": "fused", "rank_layout": "separate allocations"})
+            del sep
         del bufs, w
         torch.cuda.empty_cache()
 
     # workload 5: bf16 storage, binary32 accumulation, 40 ranks
     wl = synth.WORKLOADS[5]
     N, P = wl.N, wl.P
-    bufs = synth.rank_gradients(wl, dev)
+    bufs = synth.rank_gradients_in_pool(wl, api.rar_rank_stride(P, api.BF16), dev)
     w = synth.weights(wl, dev)
     nb = alg_bytes(N, P, 2, True)
     bf_leg = oracle_timer("ring_bf16", bufs, w, wl.lr)
@@ -402,6 +413,11 @@ def secondary_rows(dev, stream, reps=5):
         add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream),
             moved_bf_ring if algo == api.RING else None, {"algo": an}, bf_leg)
         del plan
+    sep = synth.rank_gradients(wl, dev)
+    plan = api.rar_plan(N, P, api.BF16)
+    add(f"{wl.name}_fused_separate_allocations", nb, lambda: api.rar_allreduce_sgd(plan, sep, w, wl.lr, P, stream),
+        None, {"algo": "fused", "rank_layout": "separate allocations"})
+    del sep, plan
     del bufs, w
     torch.cuda.empty_cache()
 

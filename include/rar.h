@@ -112,6 +112,19 @@ typedef enum {
  * starts as RAR_ALGO_FUSED. */
 rar_status rar_plan(int N, int64_t P, rar_dtype dtype, rar_chunking chunking, rar_plan_t *out);
 
+/* Layout advice for callers that place the N logical ranks of one device in
+ * a single allocation (rank n at base + n * stride, base 16-byte aligned):
+ * *stride_bytes receives the smallest stride >= P * element size that is
+ * 2 MiB modulo 4 MiB.  Where rank buffers start matters on MI355X; measured
+ * for the fused pass, 10 ranks x 300M fp32 with SGD, one process per box:
+ * this stride 4.17-4.39 ms; separately allocated buffers (which lie a
+ * multiple of 4 MiB apart) 4.28-4.59 ms; a stride of 1 or 3 MiB modulo
+ * 4 MiB 4.40-4.80 ms.  40 ranks x 100M bf16: 2.92 ms against 3.12 ms for
+ * separate buffers.  Results never depend on the layout.  Host only, no HIP
+ * call.  RAR_EINVAL: NULL stride_bytes, unknown dtype, P < 0, or P so large
+ * that the stride overflows. */
+rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *stride_bytes);
+
 /* Free the plan and its workspace (if any).  Waits for the device to finish
  * work that may use the workspace.  NULL is accepted. */
 rar_status rar_plan_destroy(rar_plan_t plan);

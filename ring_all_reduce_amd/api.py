@@ -110,6 +110,13 @@ def rar_plan(N: int, P: int, dtype: int = F32, chunking: int = BALANCED) -> Plan
     return Plan(out.value, int(N), int(P), int(dtype), int(chunking))
 
 
+def rar_rank_stride(P: int, dtype: int = F32) -> int:
+    """Recommended byte distance between rank buffers carved from one allocation."""
+    out = ctypes.c_int64()
+    _check(lib().rar_rank_stride(int(P), int(dtype), ctypes.byref(out)), "rar_rank_stride")
+    return out.value
+
+
 def rar_plan_destroy(plan: Plan) -> None:
     if plan.handle:
         h, plan.handle = plan.handle, ctypes.c_void_p()

@@ -275,6 +275,17 @@ extern "C" rar_status rar_plan(int N, int64_t P, rar_dtype dtype, rar_chunking c
     return RAR_OK;
 }
 
+extern "C" rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *stride_bytes)
+{
+    constexpr int64_t MiB = int64_t(1) << 20;
+    if (!stride_bytes || !valid_dtype(dtype) || P < 0 || P > (INT64_MAX - 8 * MiB) / elem_bytes(dtype))
+        return RAR_EINVAL;
+    const int64_t need = P * elem_bytes(dtype);
+    const int64_t extra = need > 2 * MiB ? need - 2 * MiB : 0;
+    *stride_bytes = 2 * MiB + (extra + 4 * MiB - 1) / (4 * MiB) * (4 * MiB);
+    return RAR_OK;
+}
+
 extern "C" rar_status rar_plan_destroy(rar_plan_t plan)
 {
     if (!plan)

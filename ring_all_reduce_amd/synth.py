@@ -101,22 +101,43 @@ def uniform_f32(P: int, seed: int, lo: float, hi: float, device="cpu"):
     return t
 
 
+def _rank_draw(wl: Workload, r: int, P: int, device):
+    s = seed_for(wl.key, r)
+    if wl.dist == "normal":
+        t = normal_f32(P, s, wl.scale, device)
+        return t if wl.dtype == "f32" else t.to(torch.bfloat16)
+    if wl.dist == "student_t3":
+        t = student_t3_bf16(P, s, wl.scale, device)
+        return t if wl.dtype == "bf16" else t.float()
+    raise ValueError(wl.dist)
+
+
 def rank_gradients(wl: Workload, device="cpu", P: Optional[int] = None, N: Optional[int] = None):
     """The N per-rank flat gradients of a workload (optionally at another P/N)."""
     P = wl.P if P is None else P
     N = wl.N if N is None else N
-    out = []
+    return [_rank_draw(wl, r, P, device) for r in range(N)]
+
+
+def rank_gradients_in_pool(wl: Workload, stride_bytes: int, device="cpu", P: Optional[int] = None,
+                           N: Optional[int] = None):
+    """The same values as rank_gradients, placed in one allocation: rank n's
+    buffer starts n * stride_bytes after the first (a layout choice only; the
+    stride is the caller's, e.g. the library's recommendation).  Returns the
+    N views; they keep the pool alive."""
+    P = wl.P if P is None else P
+    N = wl.N if N is None else N
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    es = 4 if wl.dtype == "f32" else 2
+    if stride_bytes % es or stride_bytes < P * es:
+        raise ValueError("stride must hold one rank's buffer in whole elements")
+    pool = torch.empty(max(1, (N - 1) * stride_bytes // es + P), dtype=dt, device=device)
+    views = []
     for r in range(N):
-        s = seed_for(wl.key, r)
-        if wl.dist == "normal":
-            t = normal_f32(P, s, wl.scale, device)
-            out.append(t if wl.dtype == "f32" else t.to(torch.bfloat16))
-        elif wl.dist == "student_t3":
-            t = student_t3_bf16(P, s, wl.scale, device)
-            out.append(t if wl.dtype == "bf16" else t.float())
-        else:
-            raise ValueError(wl.dist)
-    return out
+        v = pool[r * stride_bytes // es: r * stride_bytes // es + P]
+        v.copy_(_rank_draw(wl, r, P, device))
+        views.append(v)
+    return views
 
 
 def weights(wl: Workload, device="cpu", P: Optional[int] = None):

@@ -306,3 +306,20 @@ def test_bucket_layout_matches_the_oracle_on_random_lists(numels, bucket_elems, 
         for j, sg in enumerate(segs):
             assert api.rar_bucket_segment(b, k, j) == tuple(int(x) for x in sg)
         start += el
+
+
+def test_rank_stride_is_two_mib_modulo_four_and_covers_the_buffer():
+    MiB = 1 << 20
+    for P, dt in ((0, api.F32), (1, api.F32), (300_000_000, api.F32), (100_000_000, api.BF16),
+                  (524_288, api.F32), (524_289, api.F32), (1_572_864, api.F32), (1_572_865, api.F32)):
+        es = 4 if dt == api.F32 else 2
+        s = api.rar_rank_stride(P, dt)
+        assert s % (4 * MiB) == 2 * MiB and s >= P * es
+        assert s - 4 * MiB < max(P * es, 2 * MiB)  # the smallest such stride
+    assert api.rar_rank_stride(300_000_000) == 1146 * MiB
+    L = lib()
+    out = ctypes.c_int64()
+    assert L.rar_rank_stride(-1, 0, ctypes.byref(out)) == api.EINVAL
+    assert L.rar_rank_stride(10, 7, ctypes.byref(out)) == api.EINVAL
+    assert L.rar_rank_stride(10, 0, None) == api.EINVAL
+    assert L.rar_rank_stride((1 << 62), 0, ctypes.byref(out)) == api.EINVAL

@@ -1022,3 +1022,37 @@ def test_graph_capture_arena_with_ready_events():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(torch.cat(arenas).view(torch.int32), eager.view(torch.int32)), f"replay {rep} differs"
+
+
+# ---------------------------------------------------------------------------
+# Rank buffers carved from one allocation at the library's recommended stride
+# (the layout the benchmark uses): results do not depend on the layout
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("key,N,P", [(3, 10, 1_000_003), (5, 40, 400_003)])
+@pytest.mark.parametrize("algo", [api.FUSED, api.RING])
+def test_pooled_rank_layout_bit_exact(key, N, P, algo):
+    wl = synth.WORKLOADS[key]
+    dt = api.F32 if wl.dtype == "f32" else api.BF16
+    stride = api.rar_rank_stride(P, dt)
+    bufs = synth.rank_gradients_in_pool(wl, stride, DEV, P=P, N=N)
+    assert all(b.data_ptr() - bufs[0].data_ptr() == n * stride for n, b in enumerate(bufs))
+    w = synth.weights(wl, DEV, P=P)
+    if dt == api.F32:
+        ref = [b.cpu().numpy().copy() for b in bufs]
+    else:
+        ref = [b.view(torch.int16).cpu().numpy().view(np.uint16).copy() for b in bufs]
+    wr = w.cpu().numpy().copy()
+    plan = api.rar_plan(N, P, dt)
+    api.rar_plan_set_algo(plan, algo)
+    api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P)
+    torch.cuda.synchronize()
+    off = oracle.partition(N, P, api.BALANCED, 4 if dt == api.F32 else 2)
+    if dt == api.F32:
+        oracle.ring_allreduce_f32(ref, off, wr, wl.lr)
+    else:
+        oracle.ring_allreduce_bf16(ref, off, wr, wl.lr)
+    for n in range(N):
+        got = bufs[n].cpu().numpy() if dt == api.F32 else _bits16(bufs[n])
+        assert got.tobytes() == ref[n].tobytes(), f"rank {n}"
+    _assert_bits(w.cpu().numpy(), wr, "weights")
