@@ -53,5 +53,13 @@ int main(void)
     CHECK(strlen(rar_strerror(RAR_EALIGN)) > 0 && strlen(rar_strerror((rar_status)-77)) > 0);
     CHECK(rar_version() >= 100);
     printf("c abi ok\n");
+    {
+        int64_t stride = 0;
+        CHECK(rar_rank_stride(300000000, RAR_F32, &stride) == RAR_OK);
+        CHECK(stride == (int64_t)1146 << 20);
+        CHECK(stride % ((int64_t)4 << 20) == ((int64_t)2 << 20));
+        CHECK(rar_rank_stride(-1, RAR_F32, &stride) == RAR_EINVAL);
+        CHECK(rar_rank_stride(10, RAR_BF16, NULL) == RAR_EINVAL);
+    }
     return 0;
 }
