@@ -261,7 +261,8 @@ rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chunking chunk
 /* Static description of a status code; never NULL. */
 const char *rar_strerror(rar_status s);
 
-/* Library version as major*10000 + minor*100 + patch. */
+/* Library version as major*10000 + minor*100 + patch (0.2.0 = 200 adds
+ * rar_rank_stride). */
 int rar_version(void);
 
 #ifdef __cplusplus

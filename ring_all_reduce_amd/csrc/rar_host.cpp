@@ -916,4 +916,4 @@ extern "C" const char *rar_strerror(rar_status s)
     return "unknown status";
 }
 
-extern "C" int rar_version(void) { return 100; }
+extern "C" int rar_version(void) { return 200; }  // 0.2.0: rar_rank_stride added
