@@ -215,11 +215,13 @@ rar_status rar_bucket_segment(rar_buckets_t b, int bucket, int seg, int *tensor,
 
 /* Copy the bucket's segments of every rank's tensors into bucket_bufs[n]
  * (device, >= the bucket's elements).  tensors is a host array of N*n_tensors
- * device pointers, rank-major: tensors[n*n_tensors + t]. */
+ * device pointers, rank-major: tensors[n*n_tensors + t].  The N ranks' copies
+ * of a segment, and the bucket's elements of the N bucket buffers, must all be
+ * disjoint memory (RAR_EINVAL otherwise). */
 rar_status rar_bucket_pack(rar_buckets_t b, int bucket, int N, void *const tensors[],
                            void *const bucket_bufs[], void *stream);
 
-/* The reverse copy, from bucket_bufs[n] back into the tensors. */
+/* The reverse copy, from bucket_bufs[n] back into the tensors (same checks). */
 rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void *const bucket_bufs[],
                              void *const tensors[], void *stream);
 

@@ -585,6 +585,28 @@ rar_status check_bucket_args(rar_buckets_t b, int bucket, int N, void *const ten
             if (r[n].lo < r[n - 1].hi)
                 return RAR_EINVAL;
     }
+    if (!bucket_bufs)
+        return RAR_OK;
+    // the bucket's part of each bucket buffer must overlap neither the other
+    // buffers nor any segment copied to or from it (a copy launch would race)
+    const uintptr_t kb = (uintptr_t)b->elems[bucket] * es;
+    Range bb[kMaxRanks];
+    for (int n = 0; n < N; ++n)
+        bb[n] = {(uintptr_t)bucket_bufs[n], (uintptr_t)bucket_bufs[n] + kb};
+    std::sort(bb, bb + N, [](const Range &a, const Range &c) { return a.lo < c.lo; });
+    for (int n = 1; n < N; ++n)
+        if (bb[n].lo < bb[n - 1].hi)
+            return RAR_EINVAL;
+    // sorted and disjoint, so the ends ascend too: the first buffer ending
+    // after a segment starts is the only one it can overlap
+    for (const Segment &s : b->segs[bucket])
+        for (int n = 0; n < N; ++n) {
+            const uintptr_t t = (uintptr_t)tensors[(int64_t)n * b->n_tensors + s.tensor] + (uintptr_t)s.toff * es;
+            const Range seg{t, t + (uintptr_t)s.len * es};
+            const Range *m = std::upper_bound(bb, bb + N, seg.lo, [](uintptr_t x, const Range &a) { return x < a.hi; });
+            if (m != bb + N && overlaps(seg, *m))
+                return RAR_EINVAL;
+        }
     return RAR_OK;
 }
 

@@ -195,6 +195,30 @@ def test_bucket_tensors_must_not_overlap_across_ranks():
     assert L.rar_bucket_pack(b.handle, 0, 2, same, bufs, None) == api.EINVAL
 
 
+def test_bucket_buffers_must_not_overlap_each_other_or_the_tensors():
+    """Only layouts that must fail validation (FAKE is never dereferenced);
+    the tight layouts that pass are exercised on the GPU."""
+    L = lib()
+    b = api.rar_bucket_plan([100, 50], api.F32, 4 * 64)  # buckets of 64, 64, 22 elements
+    tensors = api._ptr_array([FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288])
+    far = FAKE + (1 << 30)
+    # bucket 0 needs 256 bytes per buffer: buffers 240 bytes apart overlap
+    close = api._ptr_array([far, far + 240])
+    assert L.rar_bucket_pack(b.handle, 0, 2, tensors, close, None) == api.EINVAL
+    assert L.rar_bucket_unpack(b.handle, 0, 2, close, tensors, None) == api.EINVAL
+    # bucket 2 holds 22 elements (88 bytes): 80 bytes apart overlap
+    assert L.rar_bucket_pack(b.handle, 2, 2, tensors, api._ptr_array([far, far + 80]), None) == api.EINVAL
+    # a bucket buffer over rank 1's tensor 0 (bucket 0 reads FAKE+8192 .. +256 of rank 1)
+    over = api._ptr_array([far, FAKE + 8192 + 128])
+    assert L.rar_bucket_pack(b.handle, 0, 2, tensors, over, None) == api.EINVAL
+    assert L.rar_bucket_unpack(b.handle, 0, 2, over, tensors, None) == api.EINVAL
+    # ... or starting before rank 0's tensor 0 and running into it
+    assert L.rar_bucket_pack(b.handle, 0, 2, tensors, api._ptr_array([FAKE - 128, far]), None) == api.EINVAL
+    # the packing path of the bucketed all-reduce checks the buffers too
+    assert L.rar_bucket_allreduce_mean(b.handle, 2, 0, 1, tensors, over, None) == api.EINVAL
+    assert L.rar_bucket_allreduce_mean(b.handle, 2, 0, 1, tensors, close, None) == api.EINVAL
+
+
 def test_bucket_tensors_must_not_overlap_across_tensors_or_buckets():
     """Jobs of consecutive buckets share a launch, so the direct path rejects
     any two tensors (of any ranks, in any buckets) that share memory."""

@@ -258,6 +258,47 @@ def test_bucket_pack_unpack_roundtrip_unaligned(dt):
         assert torch.equal(arenas[n], backup[n])
 
 
+def test_bucket_buffers_packed_tightly_beside_the_tensors():
+    """Bucket buffers back to back and the tensors right after them in one
+    allocation: ranges that only touch pass the overlap checks, and the
+    packing path reduces bit-exactly."""
+    N = 4
+    specs = synth.transformer_tensors(2, d=64, h=256, V=1000)
+    numels = [s.numel for s in specs]
+    bucket_bytes = 4 * 40_004
+    host = [[np.random.default_rng(700 + 100 * n + t).standard_normal(s.numel).astype(np.float32)
+             for t, s in enumerate(specs)] for n in range(N)]
+    ref = [[x.copy() for x in rank] for rank in host]
+    layout = oracle.bucketed_ring_f32(ref, bucket_bytes, api.BALANCED)
+    b = api.rar_bucket_plan(numels, api.F32, bucket_bytes)
+    nb, mx = api.rar_bucket_count(b)
+    total = sum(numels)
+    span = -(-mx // 4) * 4                        # whole 16-byte units
+    pool = torch.zeros(N * span + N * total, device=DEV)
+    bufs = [pool[n * span:(n + 1) * span] for n in range(N)]
+    arenas = [pool[N * span + n * total:N * span + (n + 1) * total] for n in range(N)]
+    for n in range(N):
+        arenas[n].copy_(torch.from_numpy(np.concatenate(host[n])))
+    starts = np.concatenate([[0], np.cumsum(numels)])
+    tensors = [[a[starts[t]:starts[t + 1]] for t in range(len(numels))] for a in arenas]
+    api.rar_bucket_allreduce_mean(b, tensors, bufs, api.BALANCED, api.RING)
+    torch.cuda.synchronize()
+    for n in range(N):
+        for t in range(len(specs)):
+            _assert_bits(tensors[n][t].cpu().numpy(), ref[n][t], f"rank {n} tensor {t}")
+    # the last (short) bucket's buffers spaced by its own size only
+    k = nb - 1
+    ek = api.rar_bucket_info(b, k)[1]
+    assert ek < mx
+    step = -(-ek // 4) * 4
+    small = [pool[n * step:n * step + ek] for n in range(N)]
+    api.rar_bucket_pack(b, k, tensors, small)
+    torch.cuda.synchronize()
+    for n in range(N):
+        for (t, toff, boff, ln) in layout[k]:
+            assert torch.equal(small[n][boff:boff + ln], tensors[n][t][toff:toff + ln])
+
+
 @pytest.mark.parametrize("mode", [api.BALANCED, api.CEIL, api.ALIGN16])
 @pytest.mark.parametrize("N", [4, 10])
 def test_bucketed_small_transformer_bit_exact(N, mode):
