@@ -1008,7 +1008,8 @@ int blocks_x(int max_blocks, int jobs, int64_t max_vecs, int vpt)
 // without SGD at 4, 8, 10, 16 and 40 ranks): binary32 gains from splitting a
 // tile over up to four groups; bf16, with twice the elements and the widening
 // per lane and a 32-byte partial sum to pass, gains from two groups at
-// 4-16 ranks and loses from any split at 40.
+// 4-16 ranks and from four at 40 (where two are far slower, and four fit in
+// the registers only with the empty asm in its hop loop).
 constexpr int groups_f32(int N) { return N <= 3 ? 1 : N <= 4 ? 2 : N <= 12 ? 4 : N <= 16 ? 3 : 4; }
 constexpr int groups_bf16(int N) { return N <= 3 ? 1 : N <= 16 ? 2 : 4; }
 
