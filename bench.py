@@ -7,7 +7,10 @@
 One step = one rar_allreduce_sgd call over the whole workload: every rank's
 gradient is averaged in ring order, the mean is written to every rank, and
 the binary32 weights take one SGD step.  Inputs are seeded synthetic vectors
-already resident in HBM when the timed region starts.
+already resident in HBM when the timed region starts.  The N ranks sit in one
+allocation at the stride rar_rank_stride_tune measures fastest among 12
+candidates (taken before the timed region); rows keep the static
+rar_rank_stride layout and separately allocated ranks beside it.
 
 Prints ONE JSON line.  `value` is GB/s of algorithmic bytes (each rank buffer
 read once and written once, w read once and written once: 2*N*P*s + 8*P) per
@@ -62,6 +65,33 @@ def kernel_sha() -> str:
 
 def alg_bytes(N, P, es, sgd):
     return 2 * N * P * es + (8 * P if sgd else 0)
+
+
+TUNE_CANDIDATES = 12
+
+
+def tuned_pool(wl, dev, stream, P=None, N=None):
+    """One allocation with room for TUNE_CANDIDATES rank strides, and the
+    stride rar_rank_stride_tune measures fastest in it (the pool is zeroed
+    first, then overwritten by the tuning passes)."""
+    import torch
+    from ring_all_reduce_amd import api, synth
+    P = wl.P if P is None else P
+    N = wl.N if N is None else N
+    dt, es = (api.F32, 4) if wl.dtype == "f32" else (api.BF16, 2)
+    MiB = 1 << 20
+    s0 = max(2 * MiB, -(-P * es // (2 * MiB)) * 2 * MiB)
+    smax = s0 + 2 * MiB * (TUNE_CANDIDATES - 1)
+    pool = torch.zeros(synth.pool_elements(wl, smax, P, N), dtype=torch.float32 if es == 4 else torch.bfloat16,
+                       device=dev)
+    stride = api.rar_rank_stride_tune(N, P, pool, dt, TUNE_CANDIDATES, stream)
+    return stride, pool
+
+
+def layout_note(stride, P, dt):
+    from ring_all_reduce_amd import api
+    return (f"one allocation, rank n at n * {stride} bytes: the fastest of {TUNE_CANDIDATES} strides timed by "
+            f"rar_rank_stride_tune (rar_rank_stride would give {api.rar_rank_stride(P, dt)})")
 
 
 def committed_traffic(workload_name: str):
@@ -143,9 +173,10 @@ def main():
     sgd = wl.lr is not None
     log(f"workload {wl.name}: N={N} P={P} dtype={wl.dtype} sgd={sgd} algo={args.algo}")
 
-    # the N logical ranks in one allocation at the library's recommended stride
-    stride = api.rar_rank_stride(P, api.F32 if es == 4 else api.BF16)
-    bufs = synth.rank_gradients_in_pool(wl, stride, dev)
+    # the N logical ranks in one allocation, at the stride the library measures fastest
+    stride, pool = tuned_pool(wl, dev, stream)
+    bufs = synth.rank_gradients_in_pool(wl, stride, dev, pool=pool)
+    log(f"rank stride {stride} bytes ({stride / (1 << 20):.0f} MiB)")
     w = synth.weights(wl, dev) if sgd else None
     plan = api.rar_plan(N, P, api.F32 if es == 4 else api.BF16, api.BALANCED)
     api.rar_plan_set_algo(plan, api.FUSED if args.algo == "fused" else api.RING)
@@ -174,6 +205,7 @@ def main():
                 api.rar_allreduce_mean(ring, bufs, P, stream)
         torch.cuda.synchronize()
         print(json.dumps({"profile_mode": True, "workload": wl.name, "launches": args.warmup + args.steps,
+                          "rank_stride": stride,
                           "copy_bytes_per_launch": cal.bytes, "kernel_src_sha256_16": kernel_sha()}))
         return
 
@@ -201,7 +233,7 @@ def main():
         "config": {"workload": wl.name, "ranks": N, "elems_per_rank": P, "op": "mean+sgd" if sgd else "mean",
                    "lr": wl.lr, "chunking": "balanced", "algo": args.algo,
                    "algorithmic_bytes_per_step": nbytes,
-                   "rank_layout": f"one allocation, rank n at n * {stride} bytes (rar_rank_stride)"},
+                   "rank_layout": layout_note(stride, P, api.F32 if es == 4 else api.BF16)},
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "device": _device_info(props),
         "params_per_s": round(P / (ms_per_step * 1e-3), 1),
@@ -220,7 +252,7 @@ def main():
             "min_launch_ms": round(min(per_ms), 5),
         },
     }
-    del bufs, w
+    del bufs, w, pool
     torch.cuda.empty_cache()
 
     if not args.no_rows:
@@ -240,7 +272,8 @@ def profile_bucketed(wl, dev, stream, iters):
     reduction over the per-rank arenas (one call each)."""
     import torch
     from ring_all_reduce_amd import api, synth
-    specs, ranks = synth.transformer_rank_tensors(wl, dev)
+    stride, pool = tuned_pool(wl, dev, stream)  # the layout the bench rows use
+    specs, ranks = synth.transformer_rank_tensors(wl, dev, pool=pool, stride_bytes=stride)
     tensors = [ts for (_, ts) in ranks]
     arenas = [flat for (flat, _) in ranks]
     b = api.rar_bucket_plan([sp.numel for sp in specs], api.F32, wl.bucket_bytes)
@@ -252,7 +285,7 @@ def profile_bucketed(wl, dev, stream, iters):
         api.rar_bucket_allreduce_arena(b, arenas, None, api.BALANCED, api.FUSED, stream)
     torch.cuda.synchronize()
     total = sum(sp.numel for sp in specs)
-    print(json.dumps({"profile_mode": True, "workload": wl.name, "calls_per_path": iters,
+    print(json.dumps({"profile_mode": True, "workload": wl.name, "calls_per_path": iters, "rank_stride": stride,
                       "algorithmic_bytes_per_call": alg_bytes(wl.N, total, 4, False),
                       "copy_bytes_per_launch": cal.bytes, "kernel_src_sha256_16": kernel_sha()}))
 
@@ -366,9 +399,11 @@ def secondary_rows(dev, stream, reps=5):
     for key in (2, 3):
         wl = synth.WORKLOADS[key]
         N, P = wl.N, wl.P
-        bufs = synth.rank_gradients_in_pool(wl, api.rar_rank_stride(P, api.F32), dev)
+        stride, pool = tuned_pool(wl, dev, stream)
+        bufs = synth.rank_gradients_in_pool(wl, stride, dev, pool=pool)
         w = synth.weights(wl, dev)
         nb = alg_bytes(N, P, 4, True)
+        lay = {"rank_layout": layout_note(stride, P, api.F32)}
         ring_leg = oracle_timer("ring_f32", bufs, w, wl.lr)
         for algo, an in ((api.FUSED, "fused"), (api.RING, "ring"), (api.NAIVE, "naive_reducer")):
             plan = api.rar_plan(N, P)
@@ -376,32 +411,44 @@ def secondary_rows(dev, stream, reps=5):
             moved = None if algo == api.FUSED else 5 * (N - 1) * P * 4 + 8 * P
             leg = oracle_timer("naive_f32", bufs, w, wl.lr) if algo == api.NAIVE else ring_leg
             add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream), moved,
-                {"algo": an}, leg)
+                {"algo": an, **lay}, leg)
         if key == 3:
             wreps = [w] + [w.clone() for _ in range(N - 1)]
             plan = api.rar_plan(N, P)
             moved = 3 * (N - 1) * P * 4 + 8 * P + 2 * (N - 1) * P * 4
             add(f"{wl.name}_reduce_scatter_sgd_allgather", nb,
                 lambda: api.rar_reduce_scatter_sgd_allgather(plan, bufs, wreps, wl.lr, P, stream), moved,
-                {"algo": "rs_sgd_ag"}, ring_leg)
-            del wreps
-            # the same call on separately allocated rank buffers (torch puts them a
-            # multiple of 4 MiB apart), for the layout's share of the difference
+                {"algo": "rs_sgd_ag", **lay}, ring_leg)
+            del wreps, bufs, pool
+            torch.cuda.empty_cache()
+            # the same call at the static stride, and on separately allocated rank
+            # buffers (torch puts them a multiple of 4 MiB apart): the layout's share
+            static = synth.rank_gradients_in_pool(wl, api.rar_rank_stride(P, api.F32), dev)
+            plan = api.rar_plan(N, P)
+            add(f"{wl.name}_fused_rar_rank_stride", nb,
+                lambda: api.rar_allreduce_sgd(plan, static, w, wl.lr, P, stream), None,
+                {"algo": "fused", "rank_layout": f"one allocation at rar_rank_stride ({api.rar_rank_stride(P)})"})
+            del static
+            torch.cuda.empty_cache()
             sep = synth.rank_gradients(wl, dev)
             plan = api.rar_plan(N, P)
             add(f"{wl.name}_fused_separate_allocations", nb,
                 lambda: api.rar_allreduce_sgd(plan, sep, w, wl.lr, P, stream), None,
                 {"algo": "fused", "rank_layout": "separate allocations"})
             del sep
-        del bufs, w
+        else:
+            del bufs, pool
+        del w
         torch.cuda.empty_cache()
 
     # workload 5: bf16 storage, binary32 accumulation, 40 ranks
     wl = synth.WORKLOADS[5]
     N, P = wl.N, wl.P
-    bufs = synth.rank_gradients_in_pool(wl, api.rar_rank_stride(P, api.BF16), dev)
+    stride, pool = tuned_pool(wl, dev, stream)
+    bufs = synth.rank_gradients_in_pool(wl, stride, dev, pool=pool)
     w = synth.weights(wl, dev)
     nb = alg_bytes(N, P, 2, True)
+    lay = {"rank_layout": layout_note(stride, P, api.BF16)}
     bf_leg = oracle_timer("ring_bf16", bufs, w, wl.lr)
     # ring steps per element: first scatter-reduce step 2+2 read, 4 written (fp32
     # workspace); each middle step 2+4 read, 4 written; last 2+4 read, 2 written,
@@ -411,19 +458,30 @@ def secondary_rows(dev, stream, reps=5):
         plan = api.rar_plan(N, P, api.BF16)
         api.rar_plan_set_algo(plan, algo)
         add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream),
-            moved_bf_ring if algo == api.RING else None, {"algo": an}, bf_leg)
+            moved_bf_ring if algo == api.RING else None, {"algo": an, **lay}, bf_leg)
         del plan
+    del bufs, pool
+    torch.cuda.empty_cache()
+    static = synth.rank_gradients_in_pool(wl, api.rar_rank_stride(P, api.BF16), dev)
+    plan = api.rar_plan(N, P, api.BF16)
+    add(f"{wl.name}_fused_rar_rank_stride", nb, lambda: api.rar_allreduce_sgd(plan, static, w, wl.lr, P, stream),
+        None, {"algo": "fused", "rank_layout": f"one allocation at rar_rank_stride ({api.rar_rank_stride(P, api.BF16)})"})
+    del static
+    torch.cuda.empty_cache()
     sep = synth.rank_gradients(wl, dev)
     plan = api.rar_plan(N, P, api.BF16)
     add(f"{wl.name}_fused_separate_allocations", nb, lambda: api.rar_allreduce_sgd(plan, sep, w, wl.lr, P, stream),
         None, {"algo": "fused", "rank_layout": "separate allocations"})
-    del sep, plan
-    del bufs, w
+    del sep, plan, w
     torch.cuda.empty_cache()
 
     # workload 4: Transformer tensor list in 25 MB buckets, 8 ranks
     wl = synth.WORKLOADS[4]
-    specs, ranks = synth.transformer_rank_tensors(wl, dev)
+    # the per-rank arenas in one allocation, at the stride measured fastest for
+    # a flat pass over arenas of this size
+    stride, pool = tuned_pool(wl, dev, stream)
+    specs, ranks = synth.transformer_rank_tensors(wl, dev, pool=pool, stride_bytes=stride)
+    lay = {"rank_layout": layout_note(stride, wl.P, api.F32)}
     tensors = [ts for (_, ts) in ranks]
     numels = [s.numel for s in specs]
     b = api.rar_bucket_plan(numels, api.F32, wl.bucket_bytes)
@@ -436,12 +494,12 @@ def secondary_rows(dev, stream, reps=5):
     # straight from the tensor lists: each bucket's segments cut at its chunk boundaries
     add(f"{wl.name}_tensor_lists_direct", nb,
         lambda: api.rar_bucket_allreduce_mean(b, tensors, None, api.BALANCED, api.FUSED, stream),
-        None, {"buckets": nbk}, bucket_leg)
+        None, {"buckets": nbk, **lay}, bucket_leg)
     # ring steps per bucket: pack into bucket buffers, 2(N-1) steps, unpack
     moved_ring = 2 * (2 * wl.N * total * 4) + 5 * (wl.N - 1) * total * 4
     add(f"{wl.name}_pack_ring_unpack", nb,
         lambda: api.rar_bucket_allreduce_mean(b, tensors, bucket_bufs, api.BALANCED, api.RING, stream),
-        moved_ring, {"buckets": nbk, "algo": "ring"}, bucket_leg)
+        moved_ring, {"buckets": nbk, "algo": "ring", **lay}, bucket_leg)
     # zero-copy: the tensors are views of one flat arena per rank, in backward
     # order, so bucket k is a slice of every arena and needs no packing
     arenas = [flat for (flat, _) in ranks]
@@ -457,10 +515,18 @@ def secondary_rows(dev, stream, reps=5):
     # one call: the buckets' chunks batched into shared launches
     add(f"{wl.name}_zero_copy_arena", nb,
         lambda: api.rar_bucket_allreduce_arena(b, arenas, None, api.BALANCED, api.FUSED, stream),
-        None, {"buckets": nbk}, bucket_leg)
+        None, {"buckets": nbk, **lay}, bucket_leg)
     # the same slices, one rar_allreduce_mean call (one launch) per bucket
-    add(f"{wl.name}_zero_copy_arena_per_bucket_calls", nb, arena_per_slice, None, {"buckets": nbk}, bucket_leg)
-    del tensors, bucket_bufs
+    add(f"{wl.name}_zero_copy_arena_per_bucket_calls", nb, arena_per_slice, None, {"buckets": nbk, **lay},
+        bucket_leg)
+    # the one-call arena path on separately allocated arenas: the layout's share
+    _, sep_ranks = synth.transformer_rank_tensors(wl, dev)
+    sep = [flat for (flat, _) in sep_ranks]
+    add(f"{wl.name}_zero_copy_arena_separate_allocations", nb,
+        lambda: api.rar_bucket_allreduce_arena(b, sep, None, api.BALANCED, api.FUSED, stream),
+        None, {"buckets": nbk, "rank_layout": "separate allocations"})
+    del sep, sep_ranks, tensors, bucket_bufs
+    torch.cuda.empty_cache()
     rows.append(overlap_row(wl, b, infos, arenas, dev, stream, nb))
     log(f"row {rows[-1]['row']}: {rows[-1]}")
     return rows

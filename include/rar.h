@@ -71,6 +71,7 @@ extern "C" {
 #endif
 
 #define RAR_MAX_RANKS 64
+#define RAR_MAX_STRIDE_CANDIDATES 64
 
 typedef struct rar_plan_s *rar_plan_t;
 typedef struct rar_buckets_s *rar_buckets_t;
@@ -120,10 +121,34 @@ rar_status rar_plan(int N, int64_t P, rar_dtype dtype, rar_chunking chunking, ra
  * this stride 4.17-4.39 ms; separately allocated buffers (which lie a
  * multiple of 4 MiB apart) 4.28-4.59 ms; a stride of 1 or 3 MiB modulo
  * 4 MiB 4.40-4.80 ms.  40 ranks x 100M bf16: 2.92 ms against 3.12 ms for
- * separate buffers.  Results never depend on the layout.  Host only, no HIP
- * call.  RAR_EINVAL: NULL stride_bytes, unknown dtype, P < 0, or P so large
- * that the stride overflows. */
+ * separate buffers.  The rule does not hold for every shape: at 8 ranks x
+ * 735M fp32 these strides are the slowest (8.1-8.4 ms against 7.5 ms for
+ * multiples of 8 MiB), because which strides are fast follows a hash of
+ * higher address bits; rar_rank_stride_tune measures instead.  Results never
+ * depend on the layout.  Host only, no HIP call.  RAR_EINVAL: NULL
+ * stride_bytes, unknown dtype, P < 0, or P so large that the stride
+ * overflows. */
 rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *stride_bytes);
+
+/* Measured layout advice for the same single-allocation placement: times the
+ * fused mean over N ranks carved from `pool` (device, 16-byte aligned,
+ * pool_bytes long) at the strides s0, s0 + 2 MiB, ... (s0 the smallest
+ * multiple of 2 MiB >= P * element size), the first max_candidates
+ * (1..RAR_MAX_STRIDE_CANDIDATES) of them for which (N-1) * stride + P *
+ * element size <= pool_bytes, and returns the fastest in *stride_bytes (each
+ * candidate: one untimed and two timed calls, in a forward and a backward
+ * round; the smallest median wins, ties to the smaller stride).  The pool's
+ * contents are overwritten; the call enqueues on `stream` and waits for it,
+ * so it must not run under graph capture.  N == 1 or P == 0 returns s0
+ * without device work.  Which strides are fast differs by shape (see
+ * rar_rank_stride); measured on MI355X, 8 ranks x 735M fp32: 7.50-7.57 ms at
+ * the pick against 7.86 ms for separate allocations and 8.35 ms for
+ * rar_rank_stride.  RAR_EINVAL: NULL stride_bytes or pool, N outside
+ * 1..RAR_MAX_RANKS, P < 0, unknown dtype, max_candidates out of range, or a
+ * pool too small for even s0.  RAR_EALIGN: pool not 16-byte aligned.
+ * RAR_EHIP / RAR_ENOMEM: a HIP call failed. */
+rar_status rar_rank_stride_tune(int N, int64_t P, rar_dtype dtype, void *pool, int64_t pool_bytes,
+                                int max_candidates, void *stream, int64_t *stride_bytes);
 
 /* Free the plan and its workspace (if any).  Waits for the device to finish
  * work that may use the workspace.  NULL is accepted. */
@@ -264,7 +289,7 @@ rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chunking chunk
 const char *rar_strerror(rar_status s);
 
 /* Library version as major*10000 + minor*100 + patch (0.2.0 = 200 adds
- * rar_rank_stride). */
+ * rar_rank_stride, 0.3.0 = 300 rar_rank_stride_tune). */
 int rar_version(void);
 
 #ifdef __cplusplus

@@ -117,6 +117,19 @@ def rar_rank_stride(P: int, dtype: int = F32) -> int:
     return out.value
 
 
+def rar_rank_stride_tune(N: int, P: int, pool, dtype: int = F32, candidates: int = 12, stream=None) -> int:
+    """Measured byte distance between rank buffers carved from `pool` (a
+    device tensor or pointer; its contents are overwritten).  Waits for the
+    stream."""
+    out = ctypes.c_int64()
+    nbytes = pool.numel() * pool.element_size() if hasattr(pool, "element_size") else None
+    if nbytes is None:
+        raise TypeError("pool must be a tensor (its size bounds the candidates)")
+    _check(lib().rar_rank_stride_tune(int(N), int(P), int(dtype), _addr(pool), int(nbytes), int(candidates),
+                                      _stream(stream), ctypes.byref(out)), "rar_rank_stride_tune")
+    return out.value
+
+
 def rar_plan_destroy(plan: Plan) -> None:
     if plan.handle:
         h, plan.handle = plan.handle, ctypes.c_void_p()

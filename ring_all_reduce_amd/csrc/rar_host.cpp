@@ -19,6 +19,7 @@
 #include "rar_internal.h"
 
 using rar::kMaxRanks;
+constexpr int kMaxStrideCandidates = RAR_MAX_STRIDE_CANDIDATES;
 
 struct rar_plan_s {
     int N = 0;
@@ -284,6 +285,90 @@ extern "C" rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *strid
     const int64_t extra = need > 2 * MiB ? need - 2 * MiB : 0;
     *stride_bytes = 2 * MiB + (extra + 4 * MiB - 1) / (4 * MiB) * (4 * MiB);
     return RAR_OK;
+}
+
+extern "C" rar_status rar_rank_stride_tune(int N, int64_t P, rar_dtype dtype, void *pool, int64_t pool_bytes,
+                                           int max_candidates, void *stream, int64_t *stride_bytes)
+{
+    constexpr int64_t MiB = int64_t(1) << 20;
+    if (!stride_bytes || N < 1 || N > kMaxRanks || P < 0 || !valid_dtype(dtype) || max_candidates < 1 ||
+        max_candidates > kMaxStrideCandidates || pool_bytes < 0 || P > (INT64_MAX / 4) / elem_bytes(dtype))
+        return RAR_EINVAL;
+    const int64_t need = P * elem_bytes(dtype);
+    // candidates: the multiples of 2 MiB from the smallest one >= need
+    const int64_t s0 = std::max<int64_t>(2 * MiB, (need + 2 * MiB - 1) / (2 * MiB) * (2 * MiB));
+    if (N == 1 || P == 0) {  // nothing to place relative to anything
+        *stride_bytes = s0;
+        return RAR_OK;
+    }
+    if (!pool)
+        return RAR_EINVAL;
+    if ((uintptr_t)pool & 15)
+        return RAR_EALIGN;
+    int K = 0;  // candidates whose N ranks fit in the pool
+    while (K < max_candidates && need <= pool_bytes && s0 + 2 * MiB * K <= (pool_bytes - need) / (N - 1))
+        ++K;
+    if (K == 0)
+        return RAR_EINVAL;
+
+    rar_plan_t pl = nullptr;
+    rar_status rc = rar_plan(N, P, dtype, RAR_CHUNK_BALANCED, &pl);
+    if (rc != RAR_OK)
+        return rc;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    for (hipEvent_t &e : ev) {
+        const hipError_t he = hipEventCreate(&e);
+        if (he != hipSuccess && rc == RAR_OK)
+            rc = hip_failed(he);
+    }
+    // two rounds, forward then backward over the candidates (so a drift in
+    // the device's speed reaches all of them alike); per candidate and round
+    // one untimed call, then two timed ones
+    constexpr int kRounds = 2, kTimed = 2;
+    float ms[kMaxStrideCandidates][kRounds * kTimed] = {};
+    void *bufs[kMaxRanks];
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int r = 0; r < kRounds && rc == RAR_OK; ++r)
+        for (int i = 0; i < K && rc == RAR_OK; ++i) {
+            const int k = r % 2 == 0 ? i : K - 1 - i;
+            for (int n = 0; n < N; ++n)
+                bufs[n] = static_cast<char *>(pool) + (int64_t)n * (s0 + 2 * MiB * k);
+            rc = rar_allreduce_mean(pl, bufs, P, stream);
+            for (int t = 0; t < kTimed && rc == RAR_OK; ++t) {
+                hipError_t he = hipEventRecord(ev[0], st);
+                if (he == hipSuccess && (rc = rar_allreduce_mean(pl, bufs, P, stream)) != RAR_OK)
+                    break;
+                if (he == hipSuccess)
+                    he = hipEventRecord(ev[1], st);
+                if (he == hipSuccess)
+                    he = hipEventSynchronize(ev[1]);
+                if (he == hipSuccess)
+                    he = hipEventElapsedTime(&ms[k][r * kTimed + t], ev[0], ev[1]);
+                if (he != hipSuccess)
+                    rc = hip_failed(he);
+            }
+        }
+    if (rc == RAR_OK) {
+        // the smallest median of the four timings (the mean of the middle
+        // two); ties go to the smaller stride
+        int best = 0;
+        float best_ms = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            float *t = ms[k];
+            std::sort(t, t + kRounds * kTimed);
+            const float med = 0.5f * (t[1] + t[2]);
+            if (k == 0 || med < best_ms) {
+                best = k;
+                best_ms = med;
+            }
+        }
+        *stride_bytes = s0 + 2 * MiB * best;
+    }
+    for (hipEvent_t e : ev)
+        if (e)
+            (void)hipEventDestroy(e);
+    rar_plan_destroy(pl);
+    return rc;
 }
 
 extern "C" rar_status rar_plan_destroy(rar_plan_t plan)
@@ -938,4 +1023,4 @@ extern "C" const char *rar_strerror(rar_status s)
     return "unknown status";
 }
 
-extern "C" int rar_version(void) { return 200; }  // 0.2.0: rar_rank_stride added
+extern "C" int rar_version(void) { return 300; }  // 0.3.0: rar_rank_stride_tune added

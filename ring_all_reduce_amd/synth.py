@@ -119,19 +119,32 @@ def rank_gradients(wl: Workload, device="cpu", P: Optional[int] = None, N: Optio
     return [_rank_draw(wl, r, P, device) for r in range(N)]
 
 
+def pool_elements(wl: Workload, stride_bytes: int, P: Optional[int] = None, N: Optional[int] = None) -> int:
+    """Elements of wl's dtype that N ranks of P elements, stride_bytes apart, span."""
+    P = wl.P if P is None else P
+    N = wl.N if N is None else N
+    es = 4 if wl.dtype == "f32" else 2
+    return max(1, (N - 1) * stride_bytes // es + P)
+
+
 def rank_gradients_in_pool(wl: Workload, stride_bytes: int, device="cpu", P: Optional[int] = None,
-                           N: Optional[int] = None):
+                           N: Optional[int] = None, pool: Optional[torch.Tensor] = None):
     """The same values as rank_gradients, placed in one allocation: rank n's
     buffer starts n * stride_bytes after the first (a layout choice only; the
-    stride is the caller's, e.g. the library's recommendation).  Returns the
-    N views; they keep the pool alive."""
+    stride is the caller's, e.g. the library's recommendation).  `pool`, if
+    given, is used instead of a new allocation (1-D, of wl's dtype, at least
+    pool_elements long).  Returns the N views; they keep the pool alive."""
     P = wl.P if P is None else P
     N = wl.N if N is None else N
     dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     es = 4 if wl.dtype == "f32" else 2
     if stride_bytes % es or stride_bytes < P * es:
         raise ValueError("stride must hold one rank's buffer in whole elements")
-    pool = torch.empty(max(1, (N - 1) * stride_bytes // es + P), dtype=dt, device=device)
+    need = pool_elements(wl, stride_bytes, P, N)
+    if pool is None:
+        pool = torch.empty(need, dtype=dt, device=device)
+    elif pool.dtype != dt or pool.dim() != 1 or pool.numel() < need:
+        raise ValueError(f"pool must be 1-D {dt} of at least {need} elements")
     views = []
     for r in range(N):
         v = pool[r * stride_bytes // es: r * stride_bytes // es + P]
@@ -192,14 +205,22 @@ def transformer_tensors(layers: int = 12, d: int = 2048, h: int = 8192, V: int =
 
 
 def transformer_rank_tensors(wl: Workload, device="cpu", layers: Optional[int] = None,
-                             d: int = 2048, h: int = 8192, V: int = 32000):
+                             d: int = 2048, h: int = 8192, V: int = 32000,
+                             pool: Optional[torch.Tensor] = None, stride_bytes: int = 0):
     """Per-rank gradient tensors (backward order) for the bucketed workload,
-    each rank drawing one stream of N(0, scale^2) values split into tensors."""
+    each rank drawing one stream of N(0, scale^2) values split into tensors.
+    Each rank's tensors are views of one flat arena: its own allocation, or,
+    with `pool` (1-D float32), the slice starting at rank * stride_bytes."""
     specs = transformer_tensors(wl.layers if layers is None else layers, d, h, V)
     total = sum(s.numel for s in specs)
+    if pool is not None and (stride_bytes % 4 or stride_bytes < 4 * total or pool.dtype != torch.float32
+                             or pool.numel() < (wl.N - 1) * stride_bytes // 4 + total):
+        raise ValueError("pool must be float32 and hold N arenas stride_bytes apart")
     ranks = []
     for r in range(wl.N):
         flat = normal_f32(total, seed_for(wl.key, r), wl.scale, device)
+        if pool is not None:  # drawn on its own, then placed: the same values either way
+            flat = pool[r * stride_bytes // 4: r * stride_bytes // 4 + total].copy_(flat)
         ts, pos = [], 0
         for s in specs:
             ts.append(flat[pos:pos + s.numel].view(s.shape))

@@ -60,6 +60,22 @@ int main(void)
         CHECK(stride % ((int64_t)4 << 20) == ((int64_t)2 << 20));
         CHECK(rar_rank_stride(-1, RAR_F32, &stride) == RAR_EINVAL);
         CHECK(rar_rank_stride(10, RAR_BF16, NULL) == RAR_EINVAL);
+        /* measured advice: every call below returns before any device work */
+        void *fake = (void *)((uintptr_t)1 << 40), *odd = (void *)(((uintptr_t)1 << 40) + 8);
+        const int64_t big = (int64_t)1 << 34, MiB = (int64_t)1 << 20;
+        CHECK(rar_rank_stride_tune(1, 1000, RAR_F32, NULL, 0, 4, NULL, &stride) == RAR_OK && stride == 2 * MiB);
+        CHECK(rar_rank_stride_tune(4, 0, RAR_F32, NULL, 0, 4, NULL, &stride) == RAR_OK && stride == 2 * MiB);
+        CHECK(rar_rank_stride_tune(1, 300000000, RAR_F32, NULL, 0, 4, NULL, &stride) == RAR_OK && stride == 1146 * MiB);
+        CHECK(rar_rank_stride_tune(4, 1000, RAR_F32, NULL, big, 4, NULL, &stride) == RAR_EINVAL);
+        CHECK(rar_rank_stride_tune(4, 1000, RAR_F32, odd, big, 4, NULL, &stride) == RAR_EALIGN);
+        CHECK(rar_rank_stride_tune(4, 1000, RAR_F32, fake, 6 * MiB, 4, NULL, &stride) == RAR_EINVAL);
+        CHECK(rar_rank_stride_tune(4, 1000, RAR_F32, fake, big, 0, NULL, &stride) == RAR_EINVAL);
+        CHECK(rar_rank_stride_tune(4, 1000, RAR_F32, fake, big, RAR_MAX_STRIDE_CANDIDATES + 1, NULL, &stride) == RAR_EINVAL);
+        CHECK(rar_rank_stride_tune(0, 1000, RAR_F32, fake, big, 4, NULL, &stride) == RAR_EINVAL);
+        CHECK(rar_rank_stride_tune(RAR_MAX_RANKS + 1, 1000, RAR_F32, fake, big, 4, NULL, &stride) == RAR_EINVAL);
+        CHECK(rar_rank_stride_tune(4, 1000, (rar_dtype)7, fake, big, 4, NULL, &stride) == RAR_EINVAL);
+        CHECK(rar_rank_stride_tune(4, -1, RAR_F32, fake, big, 4, NULL, &stride) == RAR_EINVAL);
+        CHECK(rar_rank_stride_tune(4, 1000, RAR_F32, fake, big, 4, NULL, NULL) == RAR_EINVAL);
     }
     return 0;
 }

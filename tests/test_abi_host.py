@@ -347,3 +347,34 @@ def test_rank_stride_is_two_mib_modulo_four_and_covers_the_buffer():
     assert L.rar_rank_stride(10, 7, ctypes.byref(out)) == api.EINVAL
     assert L.rar_rank_stride(10, 0, None) == api.EINVAL
     assert L.rar_rank_stride((1 << 62), 0, ctypes.byref(out)) == api.EINVAL
+
+
+def test_rank_stride_tune_validates_before_any_device_work():
+    """Only calls that must return before device work (FAKE is never
+    dereferenced); the measurement itself runs on the GPU."""
+    MiB = 1 << 20
+    L = lib()
+    out = ctypes.c_int64()
+    big = 1 << 34
+    # nothing to place: the smallest candidate, no pool needed
+    assert L.rar_rank_stride_tune(1, 300_000_000, api.F32, None, 0, 4, None, ctypes.byref(out)) == api.OK
+    assert out.value == 1146 * MiB
+    assert L.rar_rank_stride_tune(8, 0, api.BF16, None, 0, 4, None, ctypes.byref(out)) == api.OK
+    assert out.value == 2 * MiB
+    assert L.rar_rank_stride_tune(1, 100_000_000, api.BF16, None, 0, 1, None, ctypes.byref(out)) == api.OK
+    assert out.value == 192 * MiB  # 200 MB rounds up to 191 MiB, then to a multiple of 2 MiB
+    bad = [
+        (4, 1000, api.F32, None, big, 4),                          # no pool
+        (4, 1000, api.F32, FAKE, 6 * MiB, 4),                      # 3 * 2 MiB + 4000 bytes do not fit
+        (4, 1000, api.F32, FAKE, big, 0),                          # no candidates
+        (4, 1000, api.F32, FAKE, big, 65),                         # beyond RAR_MAX_STRIDE_CANDIDATES
+        (0, 1000, api.F32, FAKE, big, 4), (65, 1000, api.F32, FAKE, big, 4),
+        (4, 1000, 7, FAKE, big, 4), (4, -1, api.F32, FAKE, big, 4),
+        (4, 1 << 62, api.F32, FAKE, big, 4),
+    ]
+    for args in bad:
+        assert L.rar_rank_stride_tune(*args, None, ctypes.byref(out)) == api.EINVAL, args
+    assert L.rar_rank_stride_tune(4, 1000, api.F32, FAKE + 8, big, 4, None, ctypes.byref(out)) == api.EALIGN
+    assert L.rar_rank_stride_tune(4, 1000, api.F32, FAKE, big, 4, None, None) == api.EINVAL
+    with pytest.raises(TypeError):
+        api.rar_rank_stride_tune(4, 1000, FAKE)

@@ -1097,3 +1097,48 @@ def test_pooled_rank_layout_bit_exact(key, N, P, algo):
         got = bufs[n].cpu().numpy() if dt == api.F32 else _bits16(bufs[n])
         assert got.tobytes() == ref[n].tobytes(), f"rank {n}"
     _assert_bits(w.cpu().numpy(), wr, "weights")
+
+
+@pytest.mark.parametrize("key", [3, 5])
+def test_rank_stride_tune_picks_a_fitting_candidate_and_stays_exact(key):
+    """The measured layout advice returns one of the candidates that fit the
+    pool, and the pass in that layout is bit-exact against the oracle."""
+    MiB = 1 << 20
+    wl = synth.WORKLOADS[key]
+    dt = api.F32 if wl.dtype == "f32" else api.BF16
+    tdt = torch.float32 if dt == api.F32 else torch.bfloat16
+    es = 4 if dt == api.F32 else 2
+    N, P, K = 6, 1_000_003, 5
+    s0 = -(-P * es // (2 * MiB)) * 2 * MiB
+    cands = [s0 + 2 * MiB * k for k in range(K)]
+    pool = torch.zeros(synth.pool_elements(wl, cands[-1], P, N), dtype=tdt, device=DEV)
+    stride = api.rar_rank_stride_tune(N, P, pool, dt, candidates=K)
+    assert stride in cands
+    # more candidates asked for than fit: only those that fit are tried
+    assert api.rar_rank_stride_tune(N, P, pool, dt, candidates=K + 20) in cands
+    # a pool that holds only the first candidate, and one element less
+    exact = pool[:synth.pool_elements(wl, s0, P, N)]
+    assert api.rar_rank_stride_tune(N, P, exact, dt, candidates=K) == s0
+    with pytest.raises(api.RarError) as e:
+        api.rar_rank_stride_tune(N, P, exact[:-1], dt, candidates=K)
+    assert e.value.status == api.EINVAL
+    torch.cuda.synchronize()
+    bufs = synth.rank_gradients_in_pool(wl, stride, DEV, P=P, N=N, pool=pool)
+    w = synth.weights(wl, DEV, P=P)
+    if dt == api.F32:
+        ref = [b.cpu().numpy().copy() for b in bufs]
+    else:
+        ref = [b.view(torch.int16).cpu().numpy().view(np.uint16).copy() for b in bufs]
+    wr = w.cpu().numpy().copy()
+    plan = api.rar_plan(N, P, dt)
+    api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P)
+    torch.cuda.synchronize()
+    off = oracle.partition(N, P, api.BALANCED, es)
+    if dt == api.F32:
+        oracle.ring_allreduce_f32(ref, off, wr, wl.lr)
+    else:
+        oracle.ring_allreduce_bf16(ref, off, wr, wl.lr)
+    for n in range(N):
+        got = bufs[n].cpu().numpy() if dt == api.F32 else _bits16(bufs[n])
+        assert got.tobytes() == ref[n].tobytes(), f"rank {n}"
+    _assert_bits(w.cpu().numpy(), wr, "weights")
