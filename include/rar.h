@@ -136,8 +136,9 @@ rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *stride_bytes);
  * multiple of 2 MiB >= P * element size), the first max_candidates
  * (1..RAR_MAX_STRIDE_CANDIDATES) of them for which (N-1) * stride + P *
  * element size <= pool_bytes, and returns the fastest in *stride_bytes (each
- * candidate: one untimed and two timed calls, in a forward and a backward
- * round; the smallest median wins, ties to the smaller stride).  The pool's
+ * candidate: one untimed and two timed calls in each of four rounds, forward
+ * and backward in turn; the smallest median of the eight wins, ties to the
+ * smaller stride).  The pool's
  * contents are overwritten; the call enqueues on `stream` and waits for it,
  * so it must not run under graph capture.  N == 1 or P == 0 returns s0
  * without device work.  Which strides are fast differs by shape (see

@@ -321,10 +321,12 @@ extern "C" rar_status rar_rank_stride_tune(int N, int64_t P, rar_dtype dtype, vo
         if (he != hipSuccess && rc == RAR_OK)
             rc = hip_failed(he);
     }
-    // two rounds, forward then backward over the candidates (so a drift in
-    // the device's speed reaches all of them alike); per candidate and round
-    // one untimed call, then two timed ones
-    constexpr int kRounds = 2, kTimed = 2;
+    // four rounds, alternately forward and backward over the candidates (so a
+    // drift in the device's speed reaches all of them alike); per candidate
+    // and round one untimed call, then two timed ones.  The fast strides lie
+    // within ~1% of each other and single calls vary by about as much, so
+    // fewer samples let a middling stride win now and then.
+    constexpr int kRounds = 4, kTimed = 2;
     float ms[kMaxStrideCandidates][kRounds * kTimed] = {};
     void *bufs[kMaxRanks];
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -349,14 +351,15 @@ extern "C" rar_status rar_rank_stride_tune(int N, int64_t P, rar_dtype dtype, vo
             }
         }
     if (rc == RAR_OK) {
-        // the smallest median of the four timings (the mean of the middle
+        // the smallest median of the eight timings (the mean of the middle
         // two); ties go to the smaller stride
+        constexpr int kSamples = kRounds * kTimed;
         int best = 0;
         float best_ms = 0.0f;
         for (int k = 0; k < K; ++k) {
             float *t = ms[k];
-            std::sort(t, t + kRounds * kTimed);
-            const float med = 0.5f * (t[1] + t[2]);
+            std::sort(t, t + kSamples);
+            const float med = 0.5f * (t[kSamples / 2 - 1] + t[kSamples / 2]);
             if (k == 0 || med < best_ms) {
                 best = k;
                 best_ms = med;
