@@ -257,6 +257,10 @@ def main():
 
     if not args.no_rows:
         out["rows"] = secondary_rows(dev, stream)
+        copy = next(r for r in out["rows"] if r["row"] == "copy_1.2GB_rar_copy_kernel")
+        # the headline kernel against a plain 1 -> 1 dwordx4 copy on the same box
+        out["roofline"]["vs_measured_copy"] = {"copy_GBps": copy["alg_GBps"],
+                                               "frac": round(achieved / copy["alg_GBps"], 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, dev)
     print(json.dumps(out), flush=True)
