@@ -656,28 +656,61 @@ def oracle_timer(kind, bufs, w, lr, sample_elems=20_000_000, bucket_elems=None, 
 # ---------------------------------------------------------------------------
 
 def cpu_baseline(wl, dev, sample_P=100_000_000, min_s=10.0, max_s=30.0):
+    """The oracle timed on a sample of the workload (the first sample_P
+    elements of every rank, same seeds and distribution), and its first
+    result compared bit for bit with the library's fused pass on the same
+    pristine sample."""
     import numpy as np
+    import torch
     import oracle
-    from ring_all_reduce_amd import synth
+    from ring_all_reduce_amd import api, synth
     P = min(sample_P, wl.P)
     N = wl.N
-    g = [t.cpu().numpy() for t in synth.rank_gradients(wl, dev, P=P)]
-    w = synth.weights(wl, dev, P=P).cpu().numpy()
-    off = oracle.partition(N, P)
-    runs, t_sum = 0, 0.0
+    sgd = wl.lr is not None
+    bf16 = wl.dtype == "bf16"
+    es = 2 if bf16 else 4
+
+    def host(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16).copy() if bf16 else t.cpu().numpy().copy()
+    g = [host(t) for t in synth.rank_gradients(wl, dev, P=P)]
+    w = synth.weights(wl, dev, P=P).cpu().numpy() if sgd else None
+    off = oracle.partition(N, P, oracle.BALANCED, es)
+    run = oracle.ring_allreduce_bf16 if bf16 else oracle.ring_allreduce_f32
+    runs, t_sum, first = 0, 0.0, None
     while t_sum < min_s and runs < 200:
         t0 = time.perf_counter()
-        oracle.ring_allreduce_f32(g, off, w, wl.lr or 0.0)
+        run(g, off, w, wl.lr or 0.0)
         t_sum += time.perf_counter() - t0
         runs += 1
+        if first is None:
+            first = ([x.copy() for x in g], None if w is None else w.copy())
         if t_sum > max_s:
             break
     per = t_sum / runs
-    nb = alg_bytes(N, P, 4, wl.lr is not None)
+    nb = alg_bytes(N, P, es, sgd)
+    del g
+
+    # the library on the same pristine sample
+    gd = synth.rank_gradients(wl, dev, P=P)
+    wd = synth.weights(wl, dev, P=P) if sgd else None
+    plan = api.rar_plan(N, P, api.BF16 if bf16 else api.F32)
+    if sgd:
+        api.rar_allreduce_sgd(plan, gd, wd, wl.lr, P)
+    else:
+        api.rar_allreduce_mean(plan, gd, P)
+    torch.cuda.synchronize()
+    same = all(host(t).tobytes() == ref.tobytes() for t, ref in zip(gd, first[0]))
+    if sgd:
+        same = same and wd.cpu().numpy().tobytes() == first[1].tobytes()
+    del gd, wd
+    torch.cuda.empty_cache()
     return {"value": round(nb / per / 1e9, 3), "unit": "GB/s", "cores": oracle.get_threads(), "kind": "oracle",
-            "sample": f"{N} ranks x {P} fp32 elements per rank drawn with the workload's seeds and "
-                      f"distribution (the full workload has {wl.P}), literal ring with SGD, {runs} runs, "
-                      f"{per:.3f} s per run, {t_sum:.1f} s in all",
+            "sample": f"{N} ranks x {P} {wl.dtype} elements per rank drawn with the workload's seeds and "
+                      f"distribution (the full workload has {wl.P}), literal ring{' with SGD' if sgd else ''}, "
+                      f"{runs} runs, {per:.3f} s per run, {t_sum:.1f} s in all",
+            "parity_on_sample": {"bit_exact": bool(same),
+                                 "what": "the oracle's first run against the library's fused pass on the same "
+                                         "pristine sample, every rank and the weights"},
             "cpu": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
