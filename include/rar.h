@@ -256,7 +256,9 @@ rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void *const buc
  * bucket alone (chunk table of the bucket's size, `chunking`).
  * With RAR_ALGO_FUSED and N in {2, 4, 8, 10, 16, 40} the reduction reads and
  * writes the tensors directly (each bucket segment cut at the bucket's chunk
- * boundaries; 2*N*size bytes moved per bucket) and bucket_bufs may be NULL.
+ * boundaries, and the pieces of consecutive tensors in one chunk joined
+ * where every rank's tensors are adjacent in memory; 2*N*size bytes moved
+ * per bucket) and bucket_bufs may be NULL.
  * The jobs of consecutive buckets then share launches, so all N*n_tensors
  * tensors must be pairwise disjoint memory (RAR_EINVAL otherwise).
  * Otherwise each bucket is packed into bucket_bufs[n] (N device buffers of at

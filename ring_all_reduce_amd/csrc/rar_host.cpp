@@ -875,11 +875,16 @@ rar_status bucket_plans(rar_buckets_t b, int N, rar_chunking chunking, rar_algo 
 namespace {
 
 // Bucket k reduced in place in the tensors: each segment is cut at the
-// bucket's chunk boundaries into jobs with a uniform fold start.
+// bucket's chunk boundaries into pieces with a uniform fold start.  A piece
+// that continues the previous one (same chunk, and in every rank it starts
+// where the previous one ends: tensors that are views of one flat buffer)
+// extends it, so such tensors give the jobs of one flat arena.
 rar_status bucket_direct(rar_buckets_t b, int k, int N, const rar_plan_s *pl, void *const tensors[], JobBatch &jb)
 {
     const int es = elem_bytes(b->dtype);
-    char *first[kMaxRanks];
+    char *first[kMaxRanks], *next[kMaxRanks];
+    int64_t len = 0;  // pending job: len elements from first[], fold start c
+    int c_pending = -1;
     for (const Segment &sg : b->segs[k]) {
         for (int c = 0; c < N; ++c) {
             const int64_t lo = std::max(sg.boff, pl->ct.off[c]);
@@ -887,14 +892,26 @@ rar_status bucket_direct(rar_buckets_t b, int k, int N, const rar_plan_s *pl, vo
             if (hi <= lo)
                 continue;
             for (int n = 0; n < N; ++n)
-                first[n] = static_cast<char *>(tensors[(int64_t)n * b->n_tensors + sg.tensor]) +
-                           (sg.toff + (lo - sg.boff)) * es;
-            rar_status rc = jb.add(hi - lo, c, first);
-            if (rc != RAR_OK)
-                return rc;
+                next[n] = static_cast<char *>(tensors[(int64_t)n * b->n_tensors + sg.tensor]) +
+                          (sg.toff + (lo - sg.boff)) * es;
+            bool extends = len > 0 && c == c_pending;
+            for (int n = 0; n < N && extends; ++n)
+                extends = next[n] == first[n] + len * es;
+            if (extends) {
+                len += hi - lo;
+                continue;
+            }
+            if (len > 0) {
+                rar_status rc = jb.add(len, c_pending, first);
+                if (rc != RAR_OK)
+                    return rc;
+            }
+            std::copy(next, next + N, first);
+            len = hi - lo;
+            c_pending = c;
         }
     }
-    return RAR_OK;
+    return len > 0 ? jb.add(len, c_pending, first) : RAR_OK;
 }
 
 }  // namespace

@@ -1142,3 +1142,39 @@ def test_rank_stride_tune_picks_a_fitting_candidate_and_stays_exact(key):
         got = bufs[n].cpu().numpy() if dt == api.F32 else _bits16(bufs[n])
         assert got.tobytes() == ref[n].tobytes(), f"rank {n}"
     _assert_bits(w.cpu().numpy(), wr, "weights")
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "gap_in_one_rank", "separate"])
+def test_bucket_jobs_merge_only_across_contiguous_tensors(layout):
+    """Pieces of consecutive tensors in one chunk become one job only where
+    every rank's tensors are adjacent in memory; any layout reduces
+    bit-exactly."""
+    N = 8
+    specs = synth.transformer_tensors(1, d=64, h=256, V=500)
+    numels = [s.numel for s in specs]
+    bucket_bytes = 4 * 20_000
+    host = [[np.random.default_rng(900 + 100 * n + t).standard_normal(s.numel).astype(np.float32)
+             for t, s in enumerate(specs)] for n in range(N)]
+    ref = [[x.copy() for x in rank] for rank in host]
+    oracle.bucketed_ring_f32(ref, bucket_bytes, api.BALANCED)
+    b = api.rar_bucket_plan(numels, api.F32, bucket_bytes)
+    tensors, keep = [], []
+    for n in range(N):
+        if layout == "separate":
+            ts = [torch.from_numpy(x).to(DEV) for x in host[n]]
+        else:
+            # one flat arena; in rank 3 a 4-element gap after tensor 5
+            gap = 4 if (layout == "gap_in_one_rank" and n == 3) else 0
+            flat = torch.zeros(sum(numels) + gap, device=DEV)
+            keep.append(flat)
+            ts, pos = [], 0
+            for t, k in enumerate(numels):
+                ts.append(flat[pos:pos + k])
+                ts[-1].copy_(torch.from_numpy(host[n][t]))
+                pos += k + (gap if t == 5 else 0)
+        tensors.append(ts)
+    api.rar_bucket_allreduce_mean(b, tensors, None, api.BALANCED, api.FUSED)
+    torch.cuda.synchronize()
+    for n in range(N):
+        for t in range(len(specs)):
+            _assert_bits(tensors[n][t].cpu().numpy(), ref[n][t], f"{layout} rank {n} tensor {t}")
