@@ -1178,3 +1178,63 @@ def test_bucket_jobs_merge_only_across_contiguous_tensors(layout):
     for n in range(N):
         for t in range(len(specs)):
             _assert_bits(tensors[n][t].cpu().numpy(), ref[n][t], f"{layout} rank {n} tensor {t}")
+
+
+def _tuned_layout(wl, P, N, candidates=12):
+    """The rank placement bench.py times: one pool, the stride the library
+    measures fastest among `candidates`."""
+    MiB = 1 << 20
+    es = 4 if wl.dtype == "f32" else 2
+    s0 = -(-P * es // (2 * MiB)) * 2 * MiB
+    pool = torch.zeros(synth.pool_elements(wl, s0 + 2 * MiB * (candidates - 1), P, N),
+                       dtype=torch.float32 if es == 4 else torch.bfloat16, device=DEV)
+    stride = api.rar_rank_stride_tune(N, P, pool, api.F32 if es == 4 else api.BF16, candidates)
+    return stride, pool
+
+
+@pytest.mark.parametrize("key", [3, 5])
+def test_full_size_every_element(key):
+    """The flat workloads at full size, in the layout and launch shape the
+    benchmark times: every element of every rank, and the weights, bit-exact
+    against the oracle run over the whole workload."""
+    wl = synth.WORKLOADS[key]
+    N, P = wl.N, wl.P
+    bf16 = wl.dtype == "bf16"
+    stride, pool = _tuned_layout(wl, P, N)
+    g = synth.rank_gradients_in_pool(wl, stride, DEV, pool=pool)
+    w = synth.weights(wl, DEV)
+    ref = [_bits16(t).copy() if bf16 else t.cpu().numpy() for t in g]
+    wr = w.cpu().numpy()
+    plan = api.rar_plan(N, P, api.BF16 if bf16 else api.F32)
+    api.rar_allreduce_sgd(plan, g, w, wl.lr, P)
+    off = oracle.partition(N, P, api.BALANCED, 2 if bf16 else 4)
+    (oracle.ring_allreduce_bf16 if bf16 else oracle.ring_allreduce_f32)(ref, off, wr, wl.lr)
+    torch.cuda.synchronize()
+    for n in range(N):
+        got = _bits16(g[n]) if bf16 else g[n].cpu().numpy()
+        assert got.tobytes() == ref[n].tobytes(), f"rank {n}: first difference at {_first_diff(got, ref[n])}"
+    _assert_bits(w.cpu().numpy(), wr, "weights")
+
+
+def test_full_size_transformer_buckets_every_element():
+    """The 8-rank Transformer at full size (118 buckets of 25 MB, arenas at the
+    benchmark's tuned stride), reduced straight from the tensor lists: every
+    element of every tensor bit-exact against the oracle's bucket-by-bucket
+    literal ring."""
+    wl = synth.WORKLOADS[4]
+    stride, pool = _tuned_layout(wl, wl.P, wl.N)
+    specs, ranks = synth.transformer_rank_tensors(wl, DEV, pool=pool, stride_bytes=stride)
+    numels = [sp.numel for sp in specs]
+    starts = np.concatenate([[0], np.cumsum(numels)])
+    host = []
+    for flat, _ in ranks:
+        h = flat.cpu().numpy()
+        host.append([h[starts[t]:starts[t + 1]] for t in range(len(numels))])
+    b = api.rar_bucket_plan(numels, api.F32, wl.bucket_bytes)
+    api.rar_bucket_allreduce_mean(b, [ts for _, ts in ranks], None, api.BALANCED, api.FUSED)
+    oracle.bucketed_ring_f32(host, wl.bucket_bytes, api.BALANCED)
+    torch.cuda.synchronize()
+    for n, (flat, _) in enumerate(ranks):
+        got = flat.cpu().numpy()
+        want = np.concatenate(host[n])
+        assert got.tobytes() == want.tobytes(), f"rank {n}: first difference at {_first_diff(got, want)}"
