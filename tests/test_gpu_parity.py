@@ -1195,8 +1195,9 @@ def _tuned_layout(wl, P, N, candidates=12):
 @pytest.mark.parametrize("key", [3, 5])
 def test_full_size_every_element(key):
     """The flat workloads at full size, in the layout and launch shape the
-    benchmark times: every element of every rank, and the weights, bit-exact
-    against the oracle run over the whole workload."""
+    benchmark times, through the fused pass and through the ring steps: every
+    element of every rank, and the weights, bit-exact against the oracle run
+    over the whole workload."""
     wl = synth.WORKLOADS[key]
     N, P = wl.N, wl.P
     bf16 = wl.dtype == "bf16"
@@ -1205,15 +1206,22 @@ def test_full_size_every_element(key):
     w = synth.weights(wl, DEV)
     ref = [_bits16(t).copy() if bf16 else t.cpu().numpy() for t in g]
     wr = w.cpu().numpy()
-    plan = api.rar_plan(N, P, api.BF16 if bf16 else api.F32)
-    api.rar_allreduce_sgd(plan, g, w, wl.lr, P)
     off = oracle.partition(N, P, api.BALANCED, 2 if bf16 else 4)
     (oracle.ring_allreduce_bf16 if bf16 else oracle.ring_allreduce_f32)(ref, off, wr, wl.lr)
-    torch.cuda.synchronize()
-    for n in range(N):
-        got = _bits16(g[n]) if bf16 else g[n].cpu().numpy()
-        assert got.tobytes() == ref[n].tobytes(), f"rank {n}: first difference at {_first_diff(got, ref[n])}"
-    _assert_bits(w.cpu().numpy(), wr, "weights")
+    for algo in (api.FUSED, api.RING):
+        if algo == api.RING:  # fresh inputs in the same places
+            g = synth.rank_gradients_in_pool(wl, stride, DEV, pool=pool)
+            w = synth.weights(wl, DEV)
+        plan = api.rar_plan(N, P, api.BF16 if bf16 else api.F32)
+        api.rar_plan_set_algo(plan, algo)
+        api.rar_allreduce_sgd(plan, g, w, wl.lr, P)
+        torch.cuda.synchronize()
+        for n in range(N):
+            got = _bits16(g[n]) if bf16 else g[n].cpu().numpy()
+            assert got.tobytes() == ref[n].tobytes(), \
+                f"algo {algo} rank {n}: first difference at {_first_diff(got, ref[n])}"
+        _assert_bits(w.cpu().numpy(), wr, f"algo {algo} weights")
+        del plan
 
 
 def test_full_size_transformer_buckets_every_element():
