@@ -84,7 +84,7 @@ def tuned_pool(wl, dev, stream, P=None, N=None):
     smax = s0 + 2 * MiB * (TUNE_CANDIDATES - 1)
     pool = torch.zeros(synth.pool_elements(wl, smax, P, N), dtype=torch.float32 if es == 4 else torch.bfloat16,
                        device=dev)
-    stride = api.rar_rank_stride_tune(N, P, pool, dt, TUNE_CANDIDATES, stream)
+    stride = api.rar_rank_stride_tune(N, P, dt, pool, TUNE_CANDIDATES, stream)
     return stride, pool
 
 

@@ -117,7 +117,7 @@ def rar_rank_stride(P: int, dtype: int = F32) -> int:
     return out.value
 
 
-def rar_rank_stride_tune(N: int, P: int, pool, dtype: int = F32, candidates: int = 12, stream=None) -> int:
+def rar_rank_stride_tune(N: int, P: int, dtype: int, pool, candidates: int = 12, stream=None) -> int:
     """Measured byte distance between rank buffers carved from `pool` (a
     device tensor or pointer; its contents are overwritten).  Waits for the
     stream."""

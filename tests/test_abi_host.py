@@ -377,4 +377,4 @@ def test_rank_stride_tune_validates_before_any_device_work():
     assert L.rar_rank_stride_tune(4, 1000, api.F32, FAKE + 8, big, 4, None, ctypes.byref(out)) == api.EALIGN
     assert L.rar_rank_stride_tune(4, 1000, api.F32, FAKE, big, 4, None, None) == api.EINVAL
     with pytest.raises(TypeError):
-        api.rar_rank_stride_tune(4, 1000, FAKE)
+        api.rar_rank_stride_tune(4, 1000, api.F32, FAKE)

@@ -1112,15 +1112,15 @@ def test_rank_stride_tune_picks_a_fitting_candidate_and_stays_exact(key):
     s0 = -(-P * es // (2 * MiB)) * 2 * MiB
     cands = [s0 + 2 * MiB * k for k in range(K)]
     pool = torch.zeros(synth.pool_elements(wl, cands[-1], P, N), dtype=tdt, device=DEV)
-    stride = api.rar_rank_stride_tune(N, P, pool, dt, candidates=K)
+    stride = api.rar_rank_stride_tune(N, P, dt, pool, candidates=K)
     assert stride in cands
     # more candidates asked for than fit: only those that fit are tried
-    assert api.rar_rank_stride_tune(N, P, pool, dt, candidates=K + 20) in cands
+    assert api.rar_rank_stride_tune(N, P, dt, pool, candidates=K + 20) in cands
     # a pool that holds only the first candidate, and one element less
     exact = pool[:synth.pool_elements(wl, s0, P, N)]
-    assert api.rar_rank_stride_tune(N, P, exact, dt, candidates=K) == s0
+    assert api.rar_rank_stride_tune(N, P, dt, exact, candidates=K) == s0
     with pytest.raises(api.RarError) as e:
-        api.rar_rank_stride_tune(N, P, exact[:-1], dt, candidates=K)
+        api.rar_rank_stride_tune(N, P, dt, exact[:-1], candidates=K)
     assert e.value.status == api.EINVAL
     torch.cuda.synchronize()
     bufs = synth.rank_gradients_in_pool(wl, stride, DEV, P=P, N=N, pool=pool)
@@ -1188,7 +1188,7 @@ def _tuned_layout(wl, P, N, candidates=12):
     s0 = -(-P * es // (2 * MiB)) * 2 * MiB
     pool = torch.zeros(synth.pool_elements(wl, s0 + 2 * MiB * (candidates - 1), P, N),
                        dtype=torch.float32 if es == 4 else torch.bfloat16, device=DEV)
-    stride = api.rar_rank_stride_tune(N, P, pool, api.F32 if es == 4 else api.BF16, candidates)
+    stride = api.rar_rank_stride_tune(N, P, api.F32 if es == 4 else api.BF16, pool, candidates)
     return stride, pool
 
 
