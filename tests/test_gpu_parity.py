@@ -1246,3 +1246,21 @@ def test_full_size_transformer_buckets_every_element():
         got = flat.cpu().numpy()
         want = np.concatenate(host[n])
         assert got.tobytes() == want.tobytes(), f"rank {n}: first difference at {_first_diff(got, want)}"
+
+
+def test_readme_python_example_runs():
+    """The Python example in README.md runs as written and leaves every rank
+    holding the same mean."""
+    import pathlib
+    import re
+    text = (pathlib.Path(__file__).resolve().parents[1] / "README.md").read_text()
+    blocks = re.findall(r"```python\n(.*?)```", text, flags=re.S)
+    assert blocks, "README has no python example"
+    scope = {}
+    exec(compile(blocks[0], "README.md", "exec"), scope)
+    torch.cuda.synchronize()
+    grads, w = scope["grads"], scope["w"]
+    assert len(grads) == scope["N"]
+    for n in range(1, len(grads)):
+        assert torch.equal(grads[n], grads[0]), f"rank {n}"
+    assert torch.isfinite(w).all() and bool((w != 0).any())
