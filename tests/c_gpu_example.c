@@ -3,6 +3,8 @@
  * Integer-valued gradients keep every partial sum exact, so the expected mean
  * is the correctly rounded S/N in any order and the expected weights follow
  * from two binary32 roundings; both are computed here independently.
+ * It runs twice: on separately allocated ranks, and on ranks carved from one
+ * pool at the stride rar_rank_stride_tune picks.
  * Built by __graft_entry__.build() (gcc, C99); run by tests/test_gpu_parity.py.
  * Exit status 0: all ranks and the weights match. */
 #include <math.h>
@@ -83,11 +85,47 @@ int main(void)
         fprintf(stderr, "weights differ\n");
         bad = 1;
     }
+    /* the same ranks carved from one pool at the stride the library measures
+     * fastest among four candidates, and reduced again */
+    const int64_t MiB = (int64_t)1 << 20, s0 = 2 * MiB;  /* 400,012 bytes round up to 2 MiB */
+    const int64_t pool_bytes = (N - 1) * (s0 + 3 * 2 * MiB) + (int64_t)sizeof(float) * P;
+    char *pool;
+    int64_t stride = 0;
+    HIP_OK(hipMalloc((void **)&pool, (size_t)pool_bytes));
+    rc = rar_rank_stride_tune(N, P, RAR_F32, pool, pool_bytes, 4, NULL, &stride);
+    if (rc != RAR_OK || stride < s0 || stride > s0 + 3 * 2 * MiB || stride % (2 * MiB) != 0) {
+        fprintf(stderr, "rar_rank_stride_tune: %s, stride %lld\n", rar_strerror(rc), (long long)stride);
+        return 5;
+    }
+    void *pd[N];
+    for (int n = 0; n < N; ++n) {
+        pd[n] = pool + n * stride;
+        HIP_OK(hipMemcpy(pd[n], g[n], sizeof(float) * P, hipMemcpyHostToDevice));
+    }
+    HIP_OK(hipMemcpy(dw, w, sizeof(float) * P, hipMemcpyHostToDevice));
+    if (rar_allreduce_sgd(plan, pd, dw, lr, P, NULL) != RAR_OK)
+        return 3;
+    HIP_OK(hipDeviceSynchronize());
+    for (int n = 0; n < N; ++n) {
+        HIP_OK(hipMemcpy(out, pd[n], sizeof(float) * P, hipMemcpyDeviceToHost));
+        if (memcmp(out, mean, sizeof(float) * P) != 0) {
+            fprintf(stderr, "pooled rank %d differs from the exact mean\n", n);
+            bad = 1;
+        }
+    }
+    HIP_OK(hipMemcpy(wout, dw, sizeof(float) * P, hipMemcpyDeviceToHost));
+    if (memcmp(wout, wexp, sizeof(float) * P) != 0) {
+        fprintf(stderr, "weights differ (pooled ranks)\n");
+        bad = 1;
+    }
+
     rar_plan_destroy(plan);
     for (int n = 0; n < N; ++n)
         HIP_OK(hipFree(d[n]));
     HIP_OK(hipFree(dw));
+    HIP_OK(hipFree(pool));
     if (!bad)
-        printf("c example ok: %d ranks x %d elements, bit-exact\n", N, P);
+        printf("c example ok: %d ranks x %d elements, bit-exact (separate buffers, and pooled at a %lld MiB stride)\n",
+               N, P, (long long)(stride / MiB));
     return bad;
 }
