@@ -34,7 +34,8 @@
  * Memory and streams: every device pointer is owned by the caller and must
  * stay valid until the work enqueued on `stream` (a hipStream_t passed as
  * void*, NULL = the default stream) has finished.  Calls return after
- * enqueueing; they never synchronise.  Rank buffers, weights and bucket
+ * enqueueing; they never synchronise, except rar_rank_stride_tune, which
+ * times work on its stream and waits for it.  Rank buffers, weights and bucket
  * buffers must be 16-byte aligned; bucket tensors need only element
  * alignment.  The only device allocation is the binary32 workspace of a
  * bf16 plan set to RAR_ALGO_RING (rar_plan_set_algo, or a bucket call that
@@ -113,8 +114,9 @@ typedef enum {
  * starts as RAR_ALGO_FUSED. */
 rar_status rar_plan(int N, int64_t P, rar_dtype dtype, rar_chunking chunking, rar_plan_t *out);
 
-/* Layout advice for callers that place the N logical ranks of one device in
- * a single allocation (rank n at base + n * stride, base 16-byte aligned):
+/* Not an operation of the pages: layout advice for callers that place the N
+ * logical ranks of one device in a single allocation (rank n at base +
+ * n * stride, base 16-byte aligned):
  * *stride_bytes receives the smallest stride >= P * element size that is
  * 2 MiB modulo 4 MiB.  Where rank buffers start matters on MI355X; measured
  * for the fused pass, 10 ranks x 300M fp32 with SGD, one process per box:
@@ -130,17 +132,17 @@ rar_status rar_plan(int N, int64_t P, rar_dtype dtype, rar_chunking chunking, ra
  * overflows. */
 rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *stride_bytes);
 
-/* Measured layout advice for the same single-allocation placement: times the
- * fused mean over N ranks carved from `pool` (device, 16-byte aligned,
- * pool_bytes long) at the strides s0, s0 + 2 MiB, ... (s0 the smallest
- * multiple of 2 MiB >= P * element size), the first max_candidates
- * (1..RAR_MAX_STRIDE_CANDIDATES) of them for which (N-1) * stride + P *
- * element size <= pool_bytes, and returns the fastest in *stride_bytes (each
- * candidate: one untimed and two timed calls in each of four rounds, forward
- * and backward in turn; the smallest median of the eight wins, ties to the
- * smaller stride).  The pool's
- * contents are overwritten; the call enqueues on `stream` and waits for it,
- * so it must not run under graph capture.  N == 1 or P == 0 returns s0
+/* Not an operation of the pages either: measured layout advice for the same
+ * single-allocation placement.  Times the fused mean over N ranks carved
+ * from `pool` (device, 16-byte aligned, pool_bytes long) at the strides s0,
+ * s0 + 2 MiB, ... (s0 the smallest multiple of 2 MiB >= P * element size),
+ * the first max_candidates (1..RAR_MAX_STRIDE_CANDIDATES) of them for which
+ * (N-1) * stride + P * element size <= pool_bytes, and returns the fastest
+ * in *stride_bytes (each candidate: one untimed and two timed calls in each
+ * of four rounds, forward and backward in turn; the smallest median of the
+ * eight wins, ties to the smaller stride).  The pool's contents are
+ * overwritten; the call enqueues on `stream` and waits for it, so it must
+ * not run under graph capture.  N == 1 or P == 0 returns s0
  * without device work.  Which strides are fast differs by shape (see
  * rar_rank_stride); measured on MI355X, 8 ranks x 735M fp32: 7.50-7.57 ms at
  * the pick against 7.86 ms for separate allocations and 8.35 ms for
@@ -262,8 +264,9 @@ rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void *const buc
  * The jobs of consecutive buckets then share launches, so all N*n_tensors
  * tensors must be pairwise disjoint memory (RAR_EINVAL otherwise).
  * Otherwise each bucket is packed into bucket_bufs[n] (N device buffers of at
- * least max_bucket_elems elements, 16-byte aligned, reused by every bucket),
- * reduced with `algo`, and unpacked. */
+ * least max_bucket_elems elements, 16-byte aligned, reused by every bucket,
+ * overlapping neither each other nor the tensors: RAR_EINVAL), reduced with
+ * `algo`, and unpacked. */
 rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
                                      void *const tensors[], void *const bucket_bufs[], void *stream);
 
