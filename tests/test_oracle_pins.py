@@ -455,6 +455,24 @@ def test_bf16_is_nearest_by_brute_force():
     assert np.all((h[tie] & 1) == 0)
 
 
+def test_bf16_rounding_agrees_with_torch_conversion():
+    """An independent implementation of the same rule: torch's CPU float32 ->
+    bfloat16 conversion rounds to nearest-even.  Random bit patterns, exact
+    ties at every exponent, and the values next to them (NaN excluded: the
+    payload of a quiet NaN is not part of the rule)."""
+    import torch
+    rng = np.random.default_rng(23)
+    bits = rng.integers(0, 2 ** 32, 1_000_000, dtype=np.uint64).astype(np.uint32)
+    hi = rng.integers(0, 2 ** 16, 100_000, dtype=np.uint64).astype(np.uint32) << 16
+    ties = hi | 0x8000
+    bits = np.concatenate([bits, ties, ties - 1, ties + 1, hi])
+    f = bits.view(np.float32)
+    f = f[~np.isnan(f)]
+    ours = oracle.f32_to_bf16(f)
+    theirs = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs), f"first difference at {np.flatnonzero(ours != theirs)[:1]}"
+
+
 def test_bf16_ring_within_tolerance_of_float64_mean():
     wl = synth.WORKLOADS[5]
     N, P = 40, 20_000
