@@ -20,7 +20,7 @@ Workloads follow the shapes on the pages (short names as elsewhere):
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import List, Optional, Tuple
 
 import torch

@@ -6,7 +6,6 @@ import ctypes
 import re
 import pathlib
 
-import numpy as np
 import pytest
 
 import oracle
