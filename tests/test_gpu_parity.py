@@ -1226,9 +1226,9 @@ def test_full_size_every_element(key):
 
 def test_full_size_transformer_buckets_every_element():
     """The 8-rank Transformer at full size (118 buckets of 25 MB, arenas at the
-    benchmark's tuned stride), reduced straight from the tensor lists: every
-    element of every tensor bit-exact against the oracle's bucket-by-bucket
-    literal ring."""
+    benchmark's tuned stride), reduced straight from the tensor lists, as
+    arena slices, and packed through the ring steps: every element of every
+    tensor bit-exact against the oracle's bucket-by-bucket literal ring."""
     wl = synth.WORKLOADS[4]
     stride, pool = _tuned_layout(wl, wl.P, wl.N)
     specs, ranks = synth.transformer_rank_tensors(wl, DEV, pool=pool, stride_bytes=stride)
@@ -1238,14 +1238,26 @@ def test_full_size_transformer_buckets_every_element():
     for flat, _ in ranks:
         h = flat.cpu().numpy()
         host.append([h[starts[t]:starts[t + 1]] for t in range(len(numels))])
-    b = api.rar_bucket_plan(numels, api.F32, wl.bucket_bytes)
-    api.rar_bucket_allreduce_mean(b, [ts for _, ts in ranks], None, api.BALANCED, api.FUSED)
     oracle.bucketed_ring_f32(host, wl.bucket_bytes, api.BALANCED)
-    torch.cuda.synchronize()
-    for n, (flat, _) in enumerate(ranks):
-        got = flat.cpu().numpy()
-        want = np.concatenate(host[n])
-        assert got.tobytes() == want.tobytes(), f"rank {n}: first difference at {_first_diff(got, want)}"
+    want = [np.concatenate(h) for h in host]
+    del host
+    b = api.rar_bucket_plan(numels, api.F32, wl.bucket_bytes)
+    _, mx = api.rar_bucket_count(b)
+    for path in ("tensors", "arena", "ring"):
+        if path != "tensors":  # fresh inputs in the same places
+            specs, ranks = synth.transformer_rank_tensors(wl, DEV, pool=pool, stride_bytes=stride)
+        if path == "tensors":
+            api.rar_bucket_allreduce_mean(b, [ts for _, ts in ranks], None, api.BALANCED, api.FUSED)
+        elif path == "arena":
+            api.rar_bucket_allreduce_arena(b, [flat for flat, _ in ranks], None, api.BALANCED, api.FUSED)
+        else:
+            bufs = [torch.empty(mx, device=DEV) for _ in range(wl.N)]
+            api.rar_bucket_allreduce_mean(b, [ts for _, ts in ranks], bufs, api.BALANCED, api.RING)
+        torch.cuda.synchronize()
+        for n, (flat, _) in enumerate(ranks):
+            got = flat.cpu().numpy()
+            assert got.tobytes() == want[n].tobytes(), \
+                f"{path} rank {n}: first difference at {_first_diff(got, want[n])}"
 
 
 def test_readme_python_example_runs():
