@@ -702,15 +702,27 @@ def cpu_baseline(wl, dev, sample_P=100_000_000, min_s=10.0, max_s=30.0):
     same = all(host(t).tobytes() == ref.tobytes() for t, ref in zip(gd, first[0]))
     if sgd:
         same = same and wd.cpu().numpy().tobytes() == first[1].tobytes()
+    parity = {"bit_exact": bool(same),
+              "what": "the oracle's first run against the library's fused pass on the same pristine sample, "
+                      "every rank and the weights"}
+    if bf16:
+        # the bf16 tolerance: max |y - y*| / max |y*| against the float64 mean
+        # of the same bf16 inputs, on the first elements of every rank
+        sub = min(P, 2_000_000)
+        widen = lambda h: (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        # drawn at the sample's size and sliced (a draw of another length
+        # gives other values)
+        exact = sum(widen(host(t[:sub])) for t in synth.rank_gradients(wl, dev, P=P)) / N
+        got = widen(host(gd[0][:sub]))
+        parity["max_rel_err_vs_float64_mean"] = float(np.max(np.abs(got - exact)) / np.max(np.abs(exact)))
+        parity["max_rel_err_elements"] = f"first {sub} of every rank; tolerance 1e-2"
     del gd, wd
     torch.cuda.empty_cache()
     return {"value": round(nb / per / 1e9, 3), "unit": "GB/s", "cores": oracle.get_threads(), "kind": "oracle",
             "sample": f"{N} ranks x {P} {wl.dtype} elements per rank drawn with the workload's seeds and "
                       f"distribution (the full workload has {wl.P}), literal ring{' with SGD' if sgd else ''}, "
                       f"{runs} runs, {per:.3f} s per run, {t_sum:.1f} s in all",
-            "parity_on_sample": {"bit_exact": bool(same),
-                                 "what": "the oracle's first run against the library's fused pass on the same "
-                                         "pristine sample, every rank and the weights"},
+            "parity_on_sample": parity,
             "cpu": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
