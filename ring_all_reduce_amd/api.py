@@ -70,6 +70,29 @@ def _ranks(xs: Sequence, N: int, what: str) -> ctypes.Array:
     return _ptr_array(xs)
 
 
+def _torch_dtype(dtype: int):
+    import torch
+    return torch.float32 if dtype == F32 else torch.bfloat16
+
+
+def _check_tensor(x, what: str, dtype: int, min_numel: int) -> None:
+    """A tensor argument must have the element type the library will read and
+    write through it, and at least as many elements as it will touch (the
+    library sees only an address).  Integer addresses are taken as given."""
+    if x is None or isinstance(x, int) or not hasattr(x, "data_ptr"):
+        return
+    want = _torch_dtype(dtype)
+    if x.dtype != want:
+        raise ValueError(f"{what}: dtype {x.dtype}, expected {want}")
+    if x.numel() < min_numel:
+        raise ValueError(f"{what}: {x.numel()} elements, at least {min_numel} needed")
+
+
+def _check_ranks(xs: Sequence, what: str, dtype: int, min_numel: int) -> None:
+    for n, x in enumerate(xs):
+        _check_tensor(x, f"{what}[{n}]", dtype, min_numel)
+
+
 def _stream(s) -> int:
     if s is None:
         try:
@@ -161,18 +184,36 @@ def rar_plan_traffic(plan: Plan, rank: int):
 # All-reduce
 # ---------------------------------------------------------------------------
 
+def _check_exec(plan: Plan, bufs: Sequence, P: int) -> None:
+    # a P that differs from the plan's is the library's RAR_EMISMATCH, raised
+    # before it touches any buffer
+    if int(P) == plan.P:
+        _check_ranks(bufs, "bufs", plan.dtype, plan.P)
+
+
+def _check_weights(w, what: str, plan: Plan, P: int) -> None:
+    if int(P) == plan.P:
+        _check_tensor(w, what, F32, plan.P)
+
+
 def rar_allreduce_mean(plan: Plan, bufs: Sequence, P: int, stream=None) -> None:
+    _check_exec(plan, bufs, P)
     _check(lib().rar_allreduce_mean(plan.handle, _ranks(bufs, plan.N, "bufs"), int(P), _stream(stream)),
            "rar_allreduce_mean")
 
 
 def rar_allreduce_sgd(plan: Plan, bufs: Sequence, w, lr: float, P: int, stream=None) -> None:
+    _check_exec(plan, bufs, P)
+    _check_weights(w, "w", plan, P)
     _check(lib().rar_allreduce_sgd(plan.handle, _ranks(bufs, plan.N, "bufs"), _addr(w), ctypes.c_float(lr), int(P),
                                    _stream(stream)), "rar_allreduce_sgd")
 
 
 def rar_reduce_scatter_sgd_allgather(plan: Plan, bufs: Sequence, w_reps: Sequence, lr: float, P: int,
                                      stream=None) -> None:
+    _check_exec(plan, bufs, P)
+    for n, w in enumerate(w_reps):
+        _check_weights(w, f"w_reps[{n}]", plan, P)
     _check(lib().rar_reduce_scatter_sgd_allgather(plan.handle, _ranks(bufs, plan.N, "bufs"),
                                                   _ranks(w_reps, plan.N, "w_reps"),
                                                   ctypes.c_float(lr), int(P), _stream(stream)),
@@ -184,9 +225,10 @@ def rar_reduce_scatter_sgd_allgather(plan: Plan, bufs: Sequence, w_reps: Sequenc
 # ---------------------------------------------------------------------------
 
 class Buckets:
-    def __init__(self, handle: int, n_tensors: int, dtype: int):
+    def __init__(self, handle: int, numel: Sequence[int], dtype: int):
         self.handle = ctypes.c_void_p(handle)
-        self.n_tensors, self.dtype = n_tensors, dtype
+        self.numel = [int(n) for n in numel]
+        self.n_tensors, self.dtype, self.total = len(self.numel), dtype, sum(self.numel)
 
     def __del__(self):
         try:
@@ -200,7 +242,7 @@ def rar_bucket_plan(numel: Sequence[int], dtype: int = F32, bucket_bytes: int = 
     out = ctypes.c_void_p()
     _check(lib().rar_bucket_plan(len(numel), arr, int(dtype), int(bucket_bytes), ctypes.byref(out)),
            "rar_bucket_plan")
-    return Buckets(out.value, len(numel), int(dtype))
+    return Buckets(out.value, numel, int(dtype))
 
 
 def rar_bucket_destroy(b: Buckets) -> None:
@@ -234,12 +276,25 @@ def _rank_major(b: "Buckets", tensors: Sequence[Sequence]) -> ctypes.Array:
     for n, rank in enumerate(tensors):
         if len(rank) != b.n_tensors:
             raise ValueError(f"rank {n} lists {len(rank)} tensors; the bucket plan has {b.n_tensors}")
+        for t, x in enumerate(rank):
+            _check_tensor(x, f"tensors[{n}][{t}]", b.dtype, b.numel[t])
     flat = [x for rank in tensors for x in rank]
     return _ptr_array(flat)
 
 
+def _check_bucket_bufs(b: Buckets, bucket_bufs: Sequence, elems: int) -> None:
+    _check_ranks(bucket_bufs, "bucket_bufs", b.dtype, elems)
+
+
+def _bucket_elems(b: Buckets, bucket: int) -> int:
+    # a bad bucket index is the library's RAR_EINVAL
+    nb = rar_bucket_count(b)[0] if b.handle else 0
+    return rar_bucket_info(b, bucket)[1] if 0 <= int(bucket) < nb else 0
+
+
 def rar_bucket_pack(b: Buckets, bucket: int, tensors: Sequence[Sequence], bucket_bufs: Sequence,
                     stream=None) -> None:
+    _check_bucket_bufs(b, bucket_bufs, _bucket_elems(b, bucket))
     _check(lib().rar_bucket_pack(b.handle, int(bucket), len(tensors), _rank_major(b, tensors),
                                  _ranks(bucket_bufs, len(tensors), "bucket_bufs"), _stream(stream)),
            "rar_bucket_pack")
@@ -247,6 +302,7 @@ def rar_bucket_pack(b: Buckets, bucket: int, tensors: Sequence[Sequence], bucket
 
 def rar_bucket_unpack(b: Buckets, bucket: int, bucket_bufs: Sequence, tensors: Sequence[Sequence],
                       stream=None) -> None:
+    _check_bucket_bufs(b, bucket_bufs, _bucket_elems(b, bucket))
     _check(lib().rar_bucket_unpack(b.handle, int(bucket), len(tensors),
                                    _ranks(bucket_bufs, len(tensors), "bucket_bufs"),
                                    _rank_major(b, tensors), _stream(stream)), "rar_bucket_unpack")
@@ -256,6 +312,8 @@ def rar_bucket_allreduce_mean(b: Buckets, tensors: Sequence[Sequence], bucket_bu
                               chunking: int = BALANCED, algo: int = FUSED, stream=None) -> None:
     """bucket_bufs: N buffers of max_bucket_elems, or None when the reduction
     runs straight from the tensors (RAR_ALGO_FUSED at a supported rank count)."""
+    if bucket_bufs is not None and b.handle:
+        _check_bucket_bufs(b, bucket_bufs, rar_bucket_count(b)[1])
     bufs = None if bucket_bufs is None else _ranks(bucket_bufs, len(tensors), "bucket_bufs")
     _check(lib().rar_bucket_allreduce_mean(b.handle, len(tensors), int(chunking), int(algo),
                                            _rank_major(b, tensors), bufs, _stream(stream)),
@@ -266,6 +324,7 @@ def rar_bucket_allreduce_arena(b: Buckets, arenas: Sequence, ready_events=None, 
                                algo: int = FUSED, stream=None) -> None:
     """ready_events: None, or one entry per bucket: a torch.cuda.Event, an
     integer hipEvent_t, or None (no wait)."""
+    _check_ranks(arenas, "arenas", b.dtype, b.total)
     ev = None
     if ready_events is not None:
         nb = rar_bucket_count(b)[0]

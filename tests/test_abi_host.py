@@ -102,6 +102,60 @@ def test_execute_rejects_before_touching_the_device():
     assert L.rar_reduce_scatter_sgd_allgather(plan.handle, api._ptr_array(bufs), wdup, f, P, None) == api.EINVAL
 
 
+def test_binding_checks_tensor_dtype_and_size_before_the_call():
+    # The library sees only addresses; the binding checks a tensor's element
+    # type and length against the plan before handing its address over, so a
+    # bf16 tensor for a binary32 plan, or a short buffer, cannot make the
+    # kernels run past an allocation.  CPU tensors: the checks come first.
+    import torch
+    N, P = 3, 10
+    f32 = [torch.zeros(P) for _ in range(N)]
+    plan = api.rar_plan(N, P)
+    bplan = api.rar_plan(N, P, api.BF16)
+    w = torch.zeros(P)
+    bad = {
+        "bf16 buffer for a binary32 plan": lambda: api.rar_allreduce_mean(plan, f32[:2] + [f32[2].bfloat16()], P),
+        "binary32 buffer for a bf16 plan": lambda: api.rar_allreduce_mean(bplan, f32, P),
+        "short buffer": lambda: api.rar_allreduce_mean(plan, f32[:2] + [torch.zeros(P - 1)], P),
+        "short w": lambda: api.rar_allreduce_sgd(plan, f32, torch.zeros(P - 1), 0.1, P),
+        "float64 w": lambda: api.rar_allreduce_sgd(plan, f32, torch.zeros(P, dtype=torch.float64), 0.1, P),
+        "bf16 w": lambda: api.rar_allreduce_sgd(bplan, [t.bfloat16() for t in f32], w.bfloat16(), 0.1, P),
+        "short w replica": lambda: api.rar_reduce_scatter_sgd_allgather(plan, f32, [w, w.clone(), w[:5]], 0.1, P),
+    }
+    for what, call in bad.items():
+        with pytest.raises(ValueError):
+            call()
+    numels = [7, 0, 13]
+    b = api.rar_bucket_plan(numels, api.F32, 4 * 8)
+    nb, mx = api.rar_bucket_count(b)
+    ok = [[torch.zeros(n) for n in numels] for _ in range(N)]
+    short = [[torch.zeros(n) for n in numels] for _ in range(N - 1)] + [[torch.zeros(7), torch.zeros(0),
+                                                                           torch.zeros(12)]]
+    wrong = [[torch.zeros(n) for n in numels] for _ in range(N - 1)] + [[torch.zeros(n, dtype=torch.bfloat16)
+                                                                           for n in numels]]
+    bucket_bad = {
+        "short tensor": lambda: api.rar_bucket_allreduce_mean(b, short, None),
+        "bf16 tensor in a binary32 bucket plan": lambda: api.rar_bucket_allreduce_mean(b, wrong, None),
+        "short bucket buffer": lambda: api.rar_bucket_allreduce_mean(b, ok, [torch.zeros(mx)] * 2 + [torch.zeros(mx - 1)],
+                                                                     algo=api.RING),
+        "short pack buffer": lambda: api.rar_bucket_pack(b, 0, ok, [torch.zeros(8)] * 2 + [torch.zeros(7)]),
+        "short unpack buffer": lambda: api.rar_bucket_unpack(b, 0, [torch.zeros(8)] * 2 + [torch.zeros(7)], ok),
+        "short arena": lambda: api.rar_bucket_allreduce_arena(b, [torch.zeros(20)] * 2 + [torch.zeros(19)]),
+        "bf16 arena": lambda: api.rar_bucket_allreduce_arena(b, [torch.zeros(20, dtype=torch.bfloat16)] * 3),
+    }
+    for what, call in bucket_bad.items():
+        with pytest.raises(ValueError):
+            call()
+    # what passes the checks reaches the next one: CPU tensors are not device memory
+    for call in (lambda: api.rar_allreduce_sgd(plan, f32, w, 0.1, P),
+                 lambda: api.rar_bucket_allreduce_arena(b, [torch.zeros(20)] * 3)):
+        with pytest.raises(ValueError, match="on the GPU"):
+            call()
+    # a P that differs from the plan's is still the library's RAR_EMISMATCH
+    with pytest.raises(api.RarError):
+        api.rar_allreduce_mean(plan, [0x10000000, 0x20000000, 0x30000000], P + 1)
+
+
 def test_zero_elements_is_a_no_op():
     plan = api.rar_plan(3, 0)
     api.rar_allreduce_mean(plan, [0, 0, 0], 0, stream=0)

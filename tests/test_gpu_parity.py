@@ -205,6 +205,75 @@ def test_special_values():
             _assert_bits(d[n].cpu().numpy(), ref[n], f"algo {algo} rank {n}")
 
 
+# The SGD rounding rule w - fl(lr * m), two roundings and no fused multiply-add
+# ([Gibiansky] §The communication problem; [TrainMGPU] §Training Process, step
+# 3), on two cases whose bits are derived by hand in the oracle pins: a single
+# rank with g = 3, lr = 0.1f, w = 0.3f gives +0 (an FMA gives 2^-27), and ten
+# ranks whose integer gradients sum to 1 with lr = 0.1f, w = 0.01f give the
+# mean fl(1/10) = 0x3DCCCCCD and w = -2^-30 = 0xB0800000 (an FMA gives
+# 0xB00F5C29).  P spans vector bodies, heads and tails of every chunk.
+SGD_HAND_CASES = {
+    "one_rank": dict(N=1, grads=[3.0], lr=0.1, w=0.3, mean_bits=0x40400000, bf16_mean=0x4040, w_bits=0x00000000),
+    "ten_ranks": dict(N=10, grads=[1.0] * 9 + [-8.0], lr=0.1, w=0.01, mean_bits=0x3DCCCCCD, bf16_mean=0x3DCD,
+                      w_bits=0xB0800000),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SGD_HAND_CASES))
+@pytest.mark.parametrize("path", ["fused", "ring", "naive", "rs_sgd_ag", "bf16_fused", "bf16_ring"])
+def test_sgd_rounding_hand_cases_every_path(case, path):
+    c = SGD_HAND_CASES[case]
+    N, P, lr = c["N"], 40_013, c["lr"]
+    host = [np.full(P, v, np.float32) for v in c["grads"]]
+    w0 = np.full(P, c["w"], np.float32)
+    if path.startswith("bf16"):
+        hb = [oracle.f32_to_bf16(h) for h in host]
+        assert all(np.array_equal(oracle.bf16_to_f32(b), h) for b, h in zip(hb, host))  # exact in bf16
+        d = _bf16_dev(hb)
+        plan = api.rar_plan(N, P, api.BF16)
+        api.rar_plan_set_algo(plan, api.FUSED if path == "bf16_fused" else api.RING)
+        wd = torch.from_numpy(w0.copy()).to(DEV)
+        api.rar_allreduce_sgd(plan, d, wd, lr, P)
+        torch.cuda.synchronize()
+        ref, wr = [b.copy() for b in hb], w0.copy()
+        oracle.ring_allreduce_bf16(ref, oracle.partition(N, P, api.BALANCED, 2), wr, lr)
+        for n in range(N):
+            got = _bits16(d[n])
+            assert np.all(got == c["bf16_mean"]), f"rank {n}: {hex(int(got[0]))}"
+            assert got.tobytes() == ref[n].tobytes()
+        wg = wd.cpu().numpy()
+        assert np.all(wg.view(np.uint32) == c["w_bits"]), hex(int(wg.view(np.uint32)[0]))
+        assert wg.tobytes() == wr.tobytes()
+        return
+    d = _to_dev(host)
+    plan = api.rar_plan(N, P)
+    ref, wr = [h.copy() for h in host], w0.copy()
+    if path == "naive":
+        oracle.naive_reduce_f32(ref, wr, lr)
+    else:
+        oracle.ring_allreduce_f32(ref, oracle.partition(N, P), wr, lr)
+    if path == "rs_sgd_ag":
+        reps = [torch.from_numpy(w0.copy()).to(DEV) for _ in range(N)]
+        api.rar_reduce_scatter_sgd_allgather(plan, d, reps, lr, P)
+        torch.cuda.synchronize()
+        for n, r in enumerate(reps):
+            wg = r.cpu().numpy()
+            assert np.all(wg.view(np.uint32) == c["w_bits"]), f"replica {n}: {hex(int(wg.view(np.uint32)[0]))}"
+            assert wg.tobytes() == wr.tobytes()
+        return
+    api.rar_plan_set_algo(plan, {"fused": api.FUSED, "ring": api.RING, "naive": api.NAIVE}[path])
+    wd = torch.from_numpy(w0.copy()).to(DEV)
+    api.rar_allreduce_sgd(plan, d, wd, lr, P)
+    torch.cuda.synchronize()
+    for n in range(N):
+        got = d[n].cpu().numpy()
+        assert np.all(got.view(np.uint32) == c["mean_bits"]), f"rank {n}"
+        assert got.tobytes() == ref[n].tobytes()
+    wg = wd.cpu().numpy()
+    assert np.all(wg.view(np.uint32) == c["w_bits"]), hex(int(wg.view(np.uint32)[0]))
+    assert wg.tobytes() == wr.tobytes()
+
+
 def test_runs_on_the_given_stream():
     N, P = 8, 2_000_000
     g = _host_f32(N, P, 12)
@@ -690,7 +759,7 @@ def test_bf16_special_values(algo):
             e = int(off[c]) + i * 3
             g[(c + i) % N][e] = s
         for r in range(N):
-            g[r][int(off[c]) + 40] = 0x7F7F  # mean of equal maxima: the maximum itself
+            g[r][int(off[c]) + 40] = 0x7F7F  # four bf16 maxima overflow binary32: the mean is infinity
             g[r][int(off[c]) + 41] = 0x0001  # smallest subnormal everywhere
     w0 = np.zeros(P, np.float32)
     d = _bf16_dev(g)
@@ -709,6 +778,116 @@ def test_bf16_special_values(algo):
         assert np.array_equal(np.isnan(gf), nan), f"rank {n}: NaN positions differ"
         assert got[~nan].tobytes() == ref[n][~nan].tobytes(), f"rank {n}: first diff {_first_diff(got, ref[n])}"
     _assert_bits(wd.cpu().numpy(), wr, "weights")
+
+
+def _bf16_rounding_cases(N):
+    """bf16 rank inputs (N in {2, 4}) whose binary32 mean lands on chosen
+    bit patterns, and a label per element.  Every sum is exact in any order
+    (at most one NaN per element), so the mean does not depend on the fold.
+
+    - "tie": the mean is exactly halfway between two bf16 values, at every
+      binary32 exponent whose partial sums stay finite, with the kept bit even and
+      odd, and with the kept bits all ones (the rounding carries into the
+      exponent); and every subnormal tie.  The tie 0x7F7F8000, which would
+      round to infinity, cannot be a mean of N >= 2 finite inputs: its sum
+      would exceed the binary32 range.
+    - "near": dropped bits 0x4000 and 0xC000 (round down, round up).
+    - "overflow": the sum overflows, so the mean is infinity.
+    - "nan": one rank holds a quiet or signalling NaN with a payload.
+    Ranks: N = 2 holds (a, b); N = 4 holds (a, b, b, -b), whose sum is a + b.
+    """
+    assert N in (2, 4)
+    lg = N.bit_length() - 1
+    ops, kinds = [], []
+
+    def add(a, b, kind):
+        vals = [a, b] if N == 2 else [a, b, b, -b]
+        v32 = np.array(vals, np.float32)
+        assert np.array_equal(v32.astype(np.float64), np.array(vals)), vals
+        h = oracle.f32_to_bf16(v32)
+        assert np.array_equal(oracle.bf16_to_f32(h), v32), vals  # exact in bf16
+        ops.append(h)
+        kinds.append(kind)
+
+    # N = 4 folds a + b + b in some chunks: a + 2b = 2^(e+3) at k = 0x7F must
+    # stay finite, so e <= 124 there; N = 2 only forms a + b, so e <= 126
+    for e in range(-126, 125 if N == 4 else 127):
+        for k in (0, 1, 0x2A, 0x55, 0x7E, 0x7F):
+            a = N * 2.0 ** e * (1 + k / 128)
+            b = N * 2.0 ** (e - 8)
+            m = np.float32(np.float32(a) + np.float32(b)) / np.float32(N)
+            assert int(m.view(np.uint32)) == ((e + 127) << 23) | (k << 16) | 0x8000
+            add(a, b, "tie")
+        if e % 17 == 0:
+            a = N * 2.0 ** e * (1 + 0x33 / 128)
+            add(a, 1.5 * N * 2.0 ** (e - 8), "near")   # dropped 0xC000: rounds up
+            add(a, -1.5 * N * 2.0 ** (e - 8), "near")  # 0x33 - 1 kept, dropped 0x4000: rounds down
+    for k in range(128):  # subnormal ties: m = (k << 16 | 0x8000) * 2^-149
+        b = (N // 2) * 2.0 ** -133
+        a = k * N * 2.0 ** -133
+        m = np.float32(np.float32(a) + np.float32(b)) / np.float32(N)
+        assert int(m.view(np.uint32)) == (k << 16) | 0x8000
+        add(a, b, "tie")
+    bmax = float(oracle.bf16_to_f32(np.array([0x7F7F], np.uint16))[0])
+    add(bmax, bmax, "overflow")
+    for p in (0x7FC1, 0x7F81, 0xFFA5, 0x7FFF, 0xFFC0):
+        for r in range(N):
+            h = oracle.f32_to_bf16(np.ones(N, np.float32))
+            h[r] = p
+            ops.append(h)
+            kinds.append("nan")
+    return np.stack(ops), np.array(kinds)
+
+
+@pytest.mark.parametrize("N", [2, 4])
+@pytest.mark.parametrize("path", ["fused", "ring", "bucket_tensors", "bucket_ring"])
+def test_bf16_narrowing_ties_and_nan_payloads(N, path):
+    # Each bf16 buffer receives the binary32 mean rounded to nearest bf16,
+    # ties to even, a NaN made quiet with its sign and leading payload kept;
+    # the kernels narrow with gfx950's convert instruction, the oracle with an
+    # integer rule on the bit pattern.  The elements cycle through the cases so
+    # that every case falls in chunk heads, vector bodies and tails.
+    ops, kinds = _bf16_rounding_cases(N)
+    P = 3 * len(ops) + 11
+    idx = np.arange(P) % len(ops)
+    host = [np.ascontiguousarray(ops[idx, r]) for r in range(N)]
+    d = _bf16_dev(host)
+    if path in ("fused", "ring"):
+        plan = api.rar_plan(N, P, api.BF16)
+        api.rar_plan_set_algo(plan, api.FUSED if path == "fused" else api.RING)
+        api.rar_allreduce_mean(plan, d, P)
+    else:
+        sizes = [P // 3, 5, P - P // 3 - 5]  # three tensors, buckets of 1000 elements
+        b = api.rar_bucket_plan(sizes, api.BF16, 2 * 1000)
+        cut = np.cumsum([0] + sizes)
+        tensors = [[t[cut[i]:cut[i + 1]] for i in range(3)] for t in d]
+        nb, mx = api.rar_bucket_count(b)
+        if path == "bucket_tensors":
+            api.rar_bucket_allreduce_mean(b, tensors, None, api.BALANCED, api.FUSED)
+        else:
+            bufs = [torch.empty(mx, dtype=torch.bfloat16, device=DEV) for _ in range(N)]
+            api.rar_bucket_allreduce_mean(b, tensors, bufs, api.BALANCED, api.RING)
+    # the binary32 means the same adds give on the device, from the binary32
+    # fused pass over the widened inputs (same chunk table, same fold order)
+    f32 = _to_dev([oracle.bf16_to_f32(h) for h in host])
+    api.rar_allreduce_mean(api.rar_plan(N, P), f32, P)
+    torch.cuda.synchronize()
+    m32 = f32[0].cpu().numpy()
+    assert np.all((m32[kinds[idx] == "tie"].view(np.uint32) & 0xFFFF) == 0x8000)
+    assert np.all(np.isinf(m32[kinds[idx] == "overflow"]))
+    # the narrowing itself, NaN payloads included: bit for bit with the oracle's
+    # rule applied to the device's binary32 means
+    want = oracle.f32_to_bf16(m32)
+    ref = [h.copy() for h in host]
+    oracle.ring_allreduce_bf16(ref, oracle.partition(N, P, api.BALANCED, 2))
+    nan = kinds[idx] == "nan"
+    assert np.all(np.isnan(oracle.bf16_to_f32(want[nan])))
+    for n in range(N):
+        got = _bits16(d[n])
+        assert got.tobytes() == want.tobytes(), f"rank {n}: first diff {_first_diff(got, want)} ({kinds[idx][_first_diff(got, want)]})"
+        # and the oracle end to end, NaN payloads included: with one NaN operand
+        # both the device's and the host's binary32 adds return that NaN made quiet
+        assert got.tobytes() == ref[n].tobytes(), f"rank {n}: first diff {_first_diff(got, ref[n])}"
 
 
 @pytest.mark.parametrize("mode", [api.BALANCED, api.CEIL, api.ALIGN16])

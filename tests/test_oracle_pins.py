@@ -13,6 +13,7 @@ Sources: [Gibiansky] "Bringing HPC Techniques to Deep Learning";
 학습 1 - DP / DDP / FSDP 개념".
 """
 import json
+from fractions import Fraction
 import math
 import os
 
@@ -390,6 +391,101 @@ def test_model_averaging_equals_gradient_averaging():
     np.testing.assert_allclose(w, avg_model, rtol=0, atol=1e-8)
 
 
+# The update w - lr*mean is written on the pages without a rounding rule
+# ([Gibiansky] §The communication problem; [TrainMGPU] §Training Process,
+# step 3).  The reading taken is the literal one: the product lr*mean is one
+# binary32 operation and the difference another, each rounded to nearest even
+# (no fused multiply-add).  The pins below decide between that reading and an
+# FMA, which rounds once, with exact rational arithmetic written here.
+
+def _rne32(q: Fraction) -> float:
+    """The binary32 value nearest to the rational q, ties to even significand
+    (normal and subnormal range; exact zero maps to +0)."""
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)  # 24-bit significand; subnormals below 2^-126
+    m = a / quantum
+    n, r = divmod(m.numerator, m.denominator)
+    if 2 * r > m.denominator or (2 * r == m.denominator and n % 2 == 1):
+        n += 1
+    return sign * float(n * quantum)
+
+
+def _bits32(x) -> int:
+    return int(np.float32(x).view(np.uint32))
+
+
+def test_sgd_two_roundings_single_rank_hand_case():
+    # N = 1, so the mean is the gradient itself, g = 3.
+    #   lr = 0.1f = 13421773 * 2^-27 (0x3DCCCCCD), w = 0.3f = 10066330 * 2^-25 (0x3E99999A).
+    #   lr*g = 40265319 * 2^-27 exactly, a 26-bit integer times 2^-27; to 24 bits
+    #   that is 10066329.75 * 2^-25, which rounds to 10066330 * 2^-25 = 0.3f.
+    #   Two roundings: w - fl(lr*g) = 0.3f - 0.3f = +0 exactly.
+    #   One rounding (FMA): w - lr*g = (40265320 - 40265319) * 2^-27 = 2^-27 (0x32000000).
+    g = np.array([3.0], np.float32)
+    lr, w0 = np.float32(0.1), np.float32(0.3)
+    assert _bits32(lr) == 0x3DCCCCCD and _bits32(w0) == 0x3E99999A
+    two = _rne32(Fraction(float(w0)) - Fraction(_rne32(Fraction(float(lr)) * Fraction(3))))
+    fma = _rne32(Fraction(float(w0)) - Fraction(float(lr)) * Fraction(3))
+    assert (_bits32(two), _bits32(fma)) == (0x00000000, 0x32000000)  # the case separates the readings
+    w = np.array([w0], np.float32)
+    oracle.ring_allreduce_f32([g], oracle.partition(1, 1), w, float(lr))
+    assert _bits32(w[0]) == 0x00000000
+
+
+def test_sgd_two_roundings_ten_ranks_inexact_mean_hand_case():
+    # N = 10 ranks whose integer gradients (nine 1s and one -8) sum to S = 1 in
+    # any order, so the mean is fl(1/10), an inexact quotient.
+    #   m  = fl(1/10) = 13421773 * 2^-27 = 0x3DCCCCCD; lr = 0.1f has the same bits.
+    #   lr*m = 13421773^2 * 2^-54 = 180143990463529 * 2^-54 (48 bits); to 24 bits:
+    #          180143990463529 / 2^24 = 10737418.56..., so fl(lr*m) = 10737419 * 2^-30 = 0x3C23D70B.
+    #   w  = 0.01f = 10737418 * 2^-30 = 0x3C23D70A.
+    #   Two roundings: (10737418 - 10737419) * 2^-30 = -2^-30 = 0xB0800000, exact.
+    #   FMA: (10737418 * 2^24 - 180143990463529) * 2^-54 = -9395241 * 2^-54 = 0xB00F5C29.
+    N, P = 10, 37  # N does not divide P: chunks of 4 and 3 elements
+    bufs = [np.full(P, 1.0 if n < N - 1 else -8.0, np.float32) for n in range(N)]
+    lr = np.float32(0.1)
+    w = np.full(P, 0.01, np.float32)
+    assert _bits32(w[0]) == 0x3C23D70A
+    assert 13421773 ** 2 == 180143990463529 and 10737418 * 2 ** 24 - 13421773 ** 2 == -9395241
+    assert _bits32(_rne32(Fraction(1, 10))) == 0x3DCCCCCD
+    assert _bits32(-2.0 ** -30) == 0xB0800000 and _bits32(-9395241 * 2.0 ** -54) == 0xB00F5C29
+    oracle.ring_allreduce_f32(bufs, oracle.partition(N, P), w, float(lr))
+    for b in bufs:
+        assert np.all(b.view(np.uint32) == 0x3DCCCCCD)
+    assert np.all(w.view(np.uint32) == 0xB0800000)
+
+
+def test_sgd_update_is_two_correct_roundings_elementwise():
+    # Random weights, gradients and rates: every updated weight equals the
+    # correctly rounded difference of w and the correctly rounded product
+    # lr*m, with m the oracle's mean (itself pinned above).  An FMA reading
+    # differs on a sizeable fraction of these elements.
+    N, P = 3, 1500
+    rng = np.random.default_rng(77)
+    bufs = _rand_bufs(N, P, 78, 0.5)
+    w0 = rng.uniform(-0.05, 0.05, P).astype(np.float32)
+    lr = np.float32(0.0123)
+    w = w0.copy()
+    oracle.ring_allreduce_f32(bufs, oracle.partition(N, P), w, float(lr))
+    m = bufs[0]
+    flr = Fraction(float(lr))
+    fma_differs = 0
+    for e in range(P):
+        prod = Fraction(_rne32(flr * Fraction(float(m[e]))))
+        want = _rne32(Fraction(float(w0[e])) - prod)
+        assert _bits32(w[e]) == _bits32(want), f"element {e}"
+        fma_differs += _bits32(_rne32(Fraction(float(w0[e])) - flr * Fraction(float(m[e])))) != _bits32(want)
+    assert fma_differs > P // 20
+
+
 # ---------------------------------------------------------------------------
 # Single reducer (prior art)
 # ---------------------------------------------------------------------------
@@ -401,6 +497,17 @@ def test_naive_reducer_values():
     oracle.naive_reduce_f32(bufs)
     for b in bufs:
         assert np.array_equal(b, (S / N).astype(np.float32))
+
+
+def test_naive_reducer_update_uses_two_roundings():
+    # the ten-rank hand case above: S = 1 in any order, so the reducer's own
+    # order gives the same mean and the same -2^-30 update
+    N, P = 10, 5
+    bufs = [np.full(P, 1.0 if n < N - 1 else -8.0, np.float32) for n in range(N)]
+    w = np.full(P, 0.01, np.float32)
+    oracle.naive_reduce_f32(bufs, w, 0.1)
+    assert np.all(bufs[0].view(np.uint32) == 0x3DCCCCCD)
+    assert np.all(w.view(np.uint32) == 0xB0800000)
 
 
 # ---------------------------------------------------------------------------
