@@ -73,6 +73,9 @@ extern "C" {
 
 #define RAR_MAX_RANKS 64
 #define RAR_MAX_STRIDE_CANDIDATES 64
+/* binary32 elements of the library's static device workspace (64 MiB on each
+ * device it runs on), used by rar_allreduce_ring_noalloc */
+#define RAR_STATIC_WS_ELEMS (1 << 24)
 
 typedef struct rar_plan_s *rar_plan_t;
 typedef struct rar_buckets_s *rar_buckets_t;
@@ -101,7 +104,8 @@ typedef enum {
     RAR_EMISMATCH = -2, /* P differs from the plan's P */
     RAR_EALIGN = -3,    /* a device pointer is not 16-byte aligned */
     RAR_ENOMEM = -4,    /* host or device allocation failed */
-    RAR_EHIP = -5       /* a HIP runtime call or kernel launch failed */
+    RAR_EHIP = -5,      /* a HIP runtime call or kernel launch failed */
+    RAR_ETOOLARGE = -6  /* P exceeds the static workspace (rar_allreduce_ring_noalloc) */
 } rar_status;
 
 /* ---------------------------------------------------------------------- */
@@ -212,6 +216,24 @@ rar_status rar_reduce_scatter_sgd_allgather(rar_plan_t plan, void *const bufs[],
                                             float *const w_reps[], float lr, int64_t P,
                                             void *stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The ring
+ * algorithm of rar_allreduce_mean (w == NULL) or rar_allreduce_sgd (w != NULL)
+ * with the same arguments, results and checks, whatever algorithm the plan
+ * has selected, and with no device allocation, free or memset: a bf16 plan's
+ * binary32 partial sums go to a workspace the library holds in a static device
+ * array of RAR_STATIC_WS_ELEMS floats instead of one the plan allocates
+ * (binary32 plans need none).  Each device keeps its own copy of that array
+ * until the process ends; its address is looked up once per device, on the
+ * first call there.  Every element of the workspace that a call reads was
+ * written earlier in the same call, so nothing is cleared between calls.  All
+ * calls on one device share the array: calls on that device that overlap in
+ * time (other streams, other host threads) race and must be serialised by the
+ * caller.  `stream` must belong to the current device (RAR_EINVAL otherwise).
+ * RAR_ETOOLARGE: a bf16 plan with N > 1 and P > RAR_STATIC_WS_ELEMS. */
+rar_status rar_allreduce_ring_noalloc(rar_plan_t plan, void *const bufs[], float *w, float lr, int64_t P,
+                                      void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* Buckets: a ragged list of per-layer gradients reduced in fixed-size     */
 /* buckets ([Gibiansky] §Applying allreduce to deep learning: the          */
@@ -295,7 +317,8 @@ rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chunking chunk
 const char *rar_strerror(rar_status s);
 
 /* Library version as major*10000 + minor*100 + patch (0.2.0 = 200 adds
- * rar_rank_stride, 0.3.0 = 300 rar_rank_stride_tune). */
+ * rar_rank_stride, 0.3.0 = 300 rar_rank_stride_tune, 0.4.0 = 400
+ * rar_allreduce_ring_noalloc). */
 int rar_version(void);
 
 #ifdef __cplusplus

@@ -28,6 +28,7 @@ SIGNATURES = {
     "rar_plan_traffic": (_int, [_vp, _int, _i64p, _i64p]),
     "rar_allreduce_mean": (_int, [_vp, ctypes.POINTER(_vp), _i64, _vp]),
     "rar_allreduce_sgd": (_int, [_vp, ctypes.POINTER(_vp), _vp, ctypes.c_float, _i64, _vp]),
+    "rar_allreduce_ring_noalloc": (_int, [_vp, ctypes.POINTER(_vp), _vp, ctypes.c_float, _i64, _vp]),
     "rar_reduce_scatter_sgd_allgather": (_int, [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                                 ctypes.c_float, _i64, _vp]),
     "rar_bucket_plan": (_int, [_int, _i64p, _int, _i64, ctypes.POINTER(_vp)]),

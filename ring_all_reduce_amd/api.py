@@ -19,8 +19,9 @@ from ._lib import lib
 F32, BF16 = 0, 1
 BALANCED, CEIL, ALIGN16 = 0, 1, 2
 FUSED, RING, NAIVE = 0, 1, 2
-OK, EINVAL, EMISMATCH, EALIGN, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EMISMATCH, EALIGN, ENOMEM, EHIP, ETOOLARGE = 0, -1, -2, -3, -4, -5, -6
 MAX_RANKS = 64
+STATIC_WS_ELEMS = 1 << 24
 
 
 class RarError(RuntimeError):
@@ -207,6 +208,17 @@ def rar_allreduce_sgd(plan: Plan, bufs: Sequence, w, lr: float, P: int, stream=N
     _check_weights(w, "w", plan, P)
     _check(lib().rar_allreduce_sgd(plan.handle, _ranks(bufs, plan.N, "bufs"), _addr(w), ctypes.c_float(lr), int(P),
                                    _stream(stream)), "rar_allreduce_sgd")
+
+
+def rar_allreduce_ring_noalloc(plan: Plan, bufs: Sequence, w, lr: float, P: int, stream=None) -> None:
+    """The ring all-reduce-mean (w None) or + SGD with no device allocation:
+    a bf16 plan's partial sums use the library's static workspace."""
+    _check_exec(plan, bufs, P)
+    if w is not None:
+        _check_weights(w, "w", plan, P)
+    _check(lib().rar_allreduce_ring_noalloc(plan.handle, _ranks(bufs, plan.N, "bufs"), _addr(w),
+                                            ctypes.c_float(lr), int(P), _stream(stream)),
+           "rar_allreduce_ring_noalloc")
 
 
 def rar_reduce_scatter_sgd_allgather(plan: Plan, bufs: Sequence, w_reps: Sequence, lr: float, P: int,

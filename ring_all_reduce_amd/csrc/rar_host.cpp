@@ -505,6 +505,40 @@ extern "C" rar_status rar_reduce_scatter_sgd_allgather(rar_plan_t plan, void *co
     return run_allgather(plan, reinterpret_cast<void *const *>(w_reps), 4, st);
 }
 
+extern "C" rar_status rar_allreduce_ring_noalloc(rar_plan_t plan, void *const bufs[], float *w, float lr,
+                                                 int64_t P, void *stream)
+{
+    bool noop;
+    rar_status rc = check_exec(plan, bufs, P, &noop);
+    if (rc != RAR_OK || noop)
+        return rc;
+    if (w && (rc = check_weights(plan, bufs, w)) != RAR_OK)
+        return rc;
+    const bool need_ws = plan->dtype == RAR_BF16 && plan->N > 1;
+    if (need_ws && P > RAR_STATIC_WS_ELEMS)
+        return RAR_ETOOLARGE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rar_plan_s ring = *plan;  // the plan's table and launch cap, the ring, the static workspace
+    ring.algo = RAR_ALGO_RING;
+    ring.ws = nullptr;
+    if (need_ws) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess)
+            return hip_failed(e);
+        if (st) {
+            hipDevice_t sd = cur;
+            if ((e = hipStreamGetDevice(st, &sd)) != hipSuccess)
+                return hip_failed(e);
+            if (sd != cur)
+                return RAR_EINVAL;
+        }
+        if ((e = rar::static_workspace(cur, &ring.ws)) != hipSuccess)
+            return hip_failed(e);
+    }
+    return run_ring(&ring, bufs, w, lr, st);
+}
+
 // =============================================================================
 // Buckets ([Gibiansky] §Applying allreduce to deep learning)
 // =============================================================================
@@ -1039,8 +1073,9 @@ extern "C" const char *rar_strerror(rar_status s)
     case RAR_EALIGN: return "device pointer not 16-byte aligned";
     case RAR_ENOMEM: return "out of memory";
     case RAR_EHIP: return "HIP runtime error";
+    case RAR_ETOOLARGE: return "element count exceeds the static workspace";
     }
     return "unknown status";
 }
 
-extern "C" int rar_version(void) { return 300; }  // 0.3.0: rar_rank_stride_tune added
+extern "C" int rar_version(void) { return 400; }  // 0.4.0: rar_allreduce_ring_noalloc added

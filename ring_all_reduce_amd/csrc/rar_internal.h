@@ -92,6 +92,11 @@ hipError_t launch_sr_step(rar_dtype dt, const StepParams &p, bool first, bool la
                           int max_blocks, int64_t max_chunk, hipStream_t st);
 hipError_t launch_copy(const CopyParams &p, int max_blocks, int64_t max_job_bytes, hipStream_t st);
 hipError_t launch_pair_add(const PairParams &p, bool last, bool sgd, int max_blocks, hipStream_t st);
+// The binary32 workspace held in the library's static device array: its
+// address on `device`, which must be the current device (looked up on the
+// first call for that device, then kept).
+constexpr int kMaxDevices = 64;
+hipError_t static_workspace(int device, float **ptr);
 // Rank counts with a bucket-jobs kernel (others use pack, reduce, unpack).
 bool bucket_jobs_supported(int N);
 hipError_t launch_bucket_jobs(rar_dtype dt, int N, const JobsParams &p, int max_blocks, int64_t max_len,

@@ -29,6 +29,7 @@
 // Numerics, identical in every kernel: binary32 adds in ring order starting at
 // the chunk's own rank, one IEEE division by N, SGD as w - (lr*m) with both
 // operations rounded (contraction is off, see the pragma), subnormals kept.
+#include <mutex>
 #include <type_traits>
 
 #include <hip/hip_bf16.h>
@@ -1055,6 +1056,30 @@ hipError_t bucket_jobs_n(rar_dtype dt, const JobsParams &p, int max_blocks, int6
 }
 
 }  // namespace
+
+// The static workspace: binary32 partial sums of a bf16 ring for callers that
+// cannot allocate.  In host code `scratch` names a host-side stand-in, not
+// device memory; only the address hipGetSymbolAddress returns for the current
+// device is ever handed to a kernel.
+static __device__ __align__(256) float scratch[RAR_STATIC_WS_ELEMS];
+
+hipError_t static_workspace(int device, float **ptr)
+{
+    static std::mutex mu;
+    static float *addr[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[device] = static_cast<float *>(p);
+    }
+    *ptr = addr[device];
+    return hipSuccess;
+}
 
 bool bucket_jobs_supported(int N)
 {

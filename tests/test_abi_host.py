@@ -156,6 +156,26 @@ def test_binding_checks_tensor_dtype_and_size_before_the_call():
         api.rar_allreduce_mean(plan, [0x10000000, 0x20000000, 0x30000000], P + 1)
 
 
+def test_noalloc_ring_rejects_before_touching_the_device():
+    # checks of rar_allreduce_mean / _sgd, then the static workspace's limit,
+    # all before the first HIP call
+    L, f = lib(), ctypes.c_float(0.1)
+    big = api.STATIC_WS_ELEMS + 1
+    bplan = api.rar_plan(4, big, api.BF16)
+    bufs = api._ptr_array(_fake_bufs(4, big, 2))
+    assert L.rar_allreduce_ring_noalloc(bplan.handle, bufs, None, f, big, None) == api.ETOOLARGE
+    assert api.rar_strerror(api.ETOOLARGE) == "element count exceeds the static workspace"
+    assert L.rar_allreduce_ring_noalloc(bplan.handle, bufs, None, f, big - 1, None) == api.EMISMATCH
+    assert L.rar_allreduce_ring_noalloc(bplan.handle, None, None, f, big, None) == api.EINVAL
+    wbad = _fake_bufs(4, big, 2)[1] + 64  # inside a rank buffer
+    assert L.rar_allreduce_ring_noalloc(bplan.handle, bufs, wbad, f, big, None) == api.EINVAL
+    plan = api.rar_plan(4, 1000)
+    fb = _fake_bufs(4, 1000)
+    assert L.rar_allreduce_ring_noalloc(plan.handle, api._ptr_array(fb[:3] + [fb[3] + 4]), None, f, 1000,
+                                        None) == api.EALIGN
+    api.rar_allreduce_ring_noalloc(api.rar_plan(3, 0, api.BF16), [0, 0, 0], None, 0.1, 0, stream=0)  # no-op
+
+
 def test_zero_elements_is_a_no_op():
     plan = api.rar_plan(3, 0)
     api.rar_allreduce_mean(plan, [0, 0, 0], 0, stream=0)

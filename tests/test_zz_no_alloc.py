@@ -1,0 +1,96 @@
+"""rar_allreduce_ring_noalloc, the entry point that allocates nothing, against
+the allocating entry points it stands in for: rar_allreduce_sgd and
+rar_allreduce_mean on a plan set to RAR_ALGO_RING, whose bf16 workspace the
+plan allocates.  Two calls in a row, the second on fewer ranks and elements,
+must each give the allocating path's bits, and both must equal the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_all_reduce_amd import api
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _bf16_host(N, P, seed):
+    # normal draws scaled by 1e-3 and rounded to bf16 by torch (input generation only)
+    out = []
+    for r in range(N):
+        g = torch.Generator().manual_seed(seed + r)
+        x = (torch.randn(P, generator=g) * 1e-3).to(torch.bfloat16)
+        out.append(x.view(torch.int16).numpy().view(np.uint16).copy())
+    return out
+
+
+def _dev(host):
+    return [torch.from_numpy(h.view(np.int16).copy()).to(DEV).view(torch.bfloat16) for h in host]
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("sgd", [True, False])
+def test_noalloc_ring_matches_allocating_ring_on_two_calls(sgd):
+    lr = 1e-4
+    # the first call covers most of the static workspace; the second is smaller
+    for call, (N, P) in enumerate([(8, api.STATIC_WS_ELEMS - 12_345), (10, 1_000_003)]):
+        print(f"call {call}: N={N} P={P} sgd={sgd}", flush=True)
+        host = _bf16_host(N, P, 500 * call + 7)
+        w0 = np.random.default_rng(call).uniform(-0.02, 0.02, P).astype(np.float32)
+        # the allocating entry point: a RING plan with its own workspace
+        ref_plan = api.rar_plan(N, P, api.BF16)
+        api.rar_plan_set_algo(ref_plan, api.RING)
+        ref = _dev(host)
+        ref_w = torch.from_numpy(w0.copy()).to(DEV) if sgd else None
+        if sgd:
+            api.rar_allreduce_sgd(ref_plan, ref, ref_w, lr, P)
+        else:
+            api.rar_allreduce_mean(ref_plan, ref, P)
+        torch.cuda.synchronize()
+        # the entry point that allocates nothing, on a plan that has no workspace
+        plan = api.rar_plan(N, P, api.BF16)
+        got = _dev(host)
+        got_w = torch.from_numpy(w0.copy()).to(DEV) if sgd else None
+        torch.cuda.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        api.rar_allreduce_ring_noalloc(plan, got, got_w, lr, P)
+        torch.cuda.synchronize()
+        if call > 0:  # the array's address was looked up on the first call
+            assert torch.cuda.mem_get_info()[0] == free0
+        for n in range(N):
+            assert _bits(got[n]).tobytes() == _bits(ref[n]).tobytes(), f"call {call} rank {n}"
+        if sgd:
+            assert got_w.cpu().numpy().tobytes() == ref_w.cpu().numpy().tobytes(), f"call {call} weights"
+        if call == 1:  # and the oracle, on the smaller call
+            o = [h.copy() for h in host]
+            ow = w0.copy() if sgd else None
+            oracle.ring_allreduce_bf16(o, oracle.partition(N, P, oracle.BALANCED, 2), ow, lr)
+            for n in (0, N - 1):
+                assert _bits(got[n]).tobytes() == o[n].tobytes(), f"oracle rank {n}"
+            if sgd:
+                assert got_w.cpu().numpy().tobytes() == ow.tobytes()
+
+
+def test_noalloc_ring_binary32_and_size_limit():
+    N, P, lr = 6, 200_003, 0.01
+    rng = np.random.default_rng(3)
+    host = [rng.standard_normal(P).astype(np.float32) for _ in range(N)]
+    w0 = rng.uniform(-0.05, 0.05, P).astype(np.float32)
+    plan = api.rar_plan(N, P)
+    d = [torch.from_numpy(h.copy()).to(DEV) for h in host]
+    w = torch.from_numpy(w0.copy()).to(DEV)
+    api.rar_allreduce_ring_noalloc(plan, d, w, lr, P)
+    torch.cuda.synchronize()
+    o, ow = [h.copy() for h in host], w0.copy()
+    oracle.ring_allreduce_f32(o, oracle.partition(N, P), ow, lr)
+    for n in range(N):
+        assert d[n].cpu().numpy().tobytes() == o[n].tobytes()
+    assert w.cpu().numpy().tobytes() == ow.tobytes()
+    big = api.STATIC_WS_ELEMS + 1
+    with pytest.raises(api.RarError) as e:
+        api.rar_allreduce_ring_noalloc(api.rar_plan(2, big, api.BF16), [0x10000000, 0x10000000 + (1 << 30)], None,
+                                       0.1, big)
+    assert e.value.status == api.ETOOLARGE
