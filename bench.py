@@ -21,8 +21,10 @@ comes from committed rocprofv3 counter runs when they were taken on the current
 kernel code.  `cpu_baseline` is the CPU oracle timed on a bounded sample of the
 same workload.  `rows` measures the other paths: ring steps, the single reducer,
 reduce-scatter + owner SGD + weight all-gather, bf16, the bucketed Transformer
-(from the tensor lists, as arena slices, packed for the ring, and overlapped
-with a simulated backward pass), the small workloads as hot and cold latency,
+(from the tensor lists, fused and as ring steps, as arena slices, and overlapped
+with a simulated backward pass, on ordinary streams and with compute units
+reserved for the reduction), reference stream kernels in the fused pass's
+access pattern (the ceiling of that pattern), the small workloads as hot and cold latency,
 and plain copy / fill references.
 
 --profile-mode [--workload 3|4|5] runs only the launches the rocprofv3 counter
@@ -68,12 +70,13 @@ def alg_bytes(N, P, es, sgd):
 
 
 TUNE_CANDIDATES = 12
+TUNE_STATS = {}  # (P, dtype) -> the tuner's per-candidate measurements
 
 
 def tuned_pool(wl, dev, stream, P=None, N=None):
     """One allocation with room for TUNE_CANDIDATES rank strides, and the
-    stride rar_rank_stride_tune measures fastest in it (the pool is zeroed
-    first, then overwritten by the tuning passes)."""
+    stride rar_rank_stride_tune picks in it (the pool is zeroed first, then
+    overwritten by the tuning passes)."""
     import torch
     from ring_all_reduce_amd import api, synth
     P = wl.P if P is None else P
@@ -84,14 +87,31 @@ def tuned_pool(wl, dev, stream, P=None, N=None):
     smax = s0 + 2 * MiB * (TUNE_CANDIDATES - 1)
     pool = torch.zeros(synth.pool_elements(wl, smax, P, N), dtype=torch.float32 if es == 4 else torch.bfloat16,
                        device=dev)
-    stride = api.rar_rank_stride_tune(N, P, dt, pool, TUNE_CANDIDATES, stream)
+    stride, cands = api.rar_rank_stride_tune_stats(N, P, dt, pool, TUNE_CANDIDATES, stream)
+    TUNE_STATS[(P, dt)] = cands
     return stride, pool
 
 
-def layout_note(stride, P, dt):
+def layout_note(stride, P, dt, full=False):
+    """The rank layout and what the tuner measured: the picked and the static
+    stride's median and spread (range of the middle six of eight timings) of
+    the fused mean, and with full=True every candidate's."""
     from ring_all_reduce_amd import api
-    return (f"one allocation, rank n at n * {stride} bytes: the fastest of {TUNE_CANDIDATES} strides timed by "
-            f"rar_rank_stride_tune (rar_rank_stride would give {api.rar_rank_stride(P, dt)})")
+    static = api.rar_rank_stride(P, dt)
+    cands = TUNE_STATS.get((P, dt), [])
+    by = {c: (m, sp) for c, m, sp in cands}
+    note = {"layout": f"one allocation, rank n at n * {stride} bytes",
+            "stride_bytes": stride, "rar_rank_stride_bytes": static,
+            "pick": (f"rar_rank_stride_tune over {len(cands)} strides: the smallest median, unless "
+                     "rar_rank_stride's stride is within the larger of the two spreads")}
+    if stride in by:
+        note["picked_median_ms"], note["picked_spread_ms"] = round(by[stride][0], 4), round(by[stride][1], 4)
+    if static in by:
+        note["rar_rank_stride_median_ms"] = round(by[static][0], 4)
+        note["rar_rank_stride_spread_ms"] = round(by[static][1], 4)
+    if full:
+        note["candidates_mib_median_spread_ms"] = [[c >> 20, round(m, 4), round(sp, 4)] for c, m, sp in cands]
+    return note
 
 
 def committed_traffic(workload_name: str):
@@ -196,9 +216,14 @@ def main():
         cal = CopyCalibration(dev)
         ring = api.rar_plan(N, P, api.F32 if es == 4 else api.BF16, api.BALANCED)
         api.rar_plan_set_algo(ring, api.RING)
+        # the same streams moved in place in the fused pass's pattern (reference kernel)
+        mover = StreamRef(dev).fn(0, bufs, w, 1 if es == 4 else 2, P * es // 16, 4, stream) \
+            if sgd and N in (10, 40) else None
         for _ in range(args.warmup + args.steps):
             step()
             cal.run_once(stream)
+            if mover:
+                mover()
             if sgd:
                 api.rar_allreduce_sgd(ring, bufs, w, wl.lr, P, stream)
             else:
@@ -233,7 +258,7 @@ def main():
         "config": {"workload": wl.name, "ranks": N, "elems_per_rank": P, "op": "mean+sgd" if sgd else "mean",
                    "lr": wl.lr, "chunking": "balanced", "algo": args.algo,
                    "algorithmic_bytes_per_step": nbytes,
-                   "rank_layout": layout_note(stride, P, api.F32 if es == 4 else api.BF16)},
+                   "rank_layout": layout_note(stride, P, api.F32 if es == 4 else api.BF16, full=True)},
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "device": _device_info(props),
         "params_per_s": round(P / (ms_per_step * 1e-3), 1),
@@ -261,6 +286,12 @@ def main():
         # the headline kernel against a plain 1 -> 1 dwordx4 copy on the same box
         out["roofline"]["vs_measured_copy"] = {"copy_GBps": copy["alg_GBps"],
                                                "frac": round(achieved / copy["alg_GBps"], 4)}
+        # and against the same streams moved in the same pattern with no arithmetic
+        mover = next((r for r in out["rows"]
+                      if r["row"] == f"{wl.name}_ref_move_in_place_{N + 1}_streams_g4"), None)
+        if mover:
+            out["roofline"]["vs_same_pattern_mover"] = {"row": mover["row"], "mover_GBps": mover["alg_GBps"],
+                                                        "frac": round(achieved / mover["alg_GBps"], 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, dev)
     print(json.dumps(out), flush=True)
@@ -292,6 +323,58 @@ def profile_bucketed(wl, dev, stream, iters):
     print(json.dumps({"profile_mode": True, "workload": wl.name, "calls_per_path": iters, "rank_stride": stride,
                       "algorithmic_bytes_per_call": alg_bytes(wl.N, total, 4, False),
                       "copy_bytes_per_launch": cal.bytes, "kernel_src_sha256_16": kernel_sha()}))
+
+
+class StreamRef:
+    """The benchmark's reference stream kernels (libstream_ref.so, not part of
+    the path): the grouped fused pass's access pattern -- 256-lane groups, one
+    16-byte vector per lane and rank, one tile per workgroup, the last group
+    also carrying the weight stream -- with no arithmetic.  Mode 0 reads every
+    stream and writes it back in place (the fused pass's bytes and streams),
+    mode 1 only writes, mode 2 only reads."""
+
+    def __init__(self, dev):
+        import ctypes
+        import torch
+        self.L = ctypes.CDLL(str(ROOT / "ring_all_reduce_amd" / "libstream_ref.so"))
+        self.L.sref_run.restype = ctypes.c_int
+        self.L.sref_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        self.sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+
+    def fn(self, mode, ranks, w, w_vpl, vecs, groups, stream):
+        import ctypes
+        arr = (ctypes.c_void_p * len(ranks))(*[t.data_ptr() for t in ranks])
+        wp = w.data_ptr() if w is not None else None
+        args = (mode, len(ranks), arr, wp, w_vpl, vecs, groups, self.sink.data_ptr(), stream.cuda_stream)
+
+        def run():
+            rc = self.L.sref_run(*args)
+            if rc != 0:
+                raise RuntimeError(f"sref_run{args[:2]}: {rc}")
+        return run
+
+
+def stream_ref_rows(add, name, ranks, w, w_vpl, vecs, groups, stream, dev):
+    """Reference rows over the workload's own buffers (in this order: the
+    write-only row overwrites them)."""
+    ref = StreamRef(dev)
+    n = len(ranks) + (1 if w is not None else 0)
+    rank_bytes = vecs * 16
+    both = 2 * (len(ranks) * rank_bytes + (w_vpl * vecs * 16 if w is not None else 0))
+    what = {"what": "reference kernel, not the path: the fused pass's streams and access pattern without its "
+                    "arithmetic"}
+    add(f"{name}_ref_move_in_place_{n}_streams_g{groups}", both, ref.fn(0, ranks, w, w_vpl, vecs, groups, stream),
+        None, what)
+    if groups != 1 and len(ranks) == 10:
+        add(f"{name}_ref_move_in_place_{n}_streams_g1", both, ref.fn(0, ranks, w, w_vpl, vecs, 1, stream), None,
+            {"what": "reference kernel: as above, every lane moving all streams"})
+    add(f"{name}_ref_move_in_place_1_stream", 2 * rank_bytes, ref.fn(0, ranks[:1], None, 0, vecs, 1, stream), None,
+        {"what": "reference kernel: one stream read and written back in place"})
+    add(f"{name}_ref_read_only_{n}_streams_g{groups}", both // 2, ref.fn(2, ranks, w, w_vpl, vecs, groups, stream),
+        None, what)
+    add(f"{name}_ref_write_only_{n}_streams_g{groups}", both // 2, ref.fn(1, ranks, w, w_vpl, vecs, groups, stream),
+        None, what)
 
 
 class CopyCalibration:
@@ -423,7 +506,11 @@ def secondary_rows(dev, stream, reps=5):
             add(f"{wl.name}_reduce_scatter_sgd_allgather", nb,
                 lambda: api.rar_reduce_scatter_sgd_allgather(plan, bufs, wreps, wl.lr, P, stream), moved,
                 {"algo": "rs_sgd_ag", **lay}, ring_leg)
-            del wreps, bufs, pool
+            del wreps
+            # the ceiling of the fused pass's access pattern on these buffers
+            stream_ref_rows(add, wl.name, bufs, w, 1, P * 4 // 16, 4, stream, dev)
+            w = synth.weights(wl, dev)
+            del bufs, pool
             torch.cuda.empty_cache()
             # the same call at the static stride, and on separately allocated rank
             # buffers (torch puts them a multiple of 4 MiB apart): the layout's share
@@ -464,6 +551,8 @@ def secondary_rows(dev, stream, reps=5):
         add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream),
             moved_bf_ring if algo == api.RING else None, {"algo": an, **lay}, bf_leg)
         del plan
+    stream_ref_rows(add, wl.name, bufs, w, 2, P * 2 // 16, 4, stream, dev)
+    w = synth.weights(wl, dev)
     del bufs, pool
     torch.cuda.empty_cache()
     static = synth.rank_gradients_in_pool(wl, api.rar_rank_stride(P, api.BF16), dev)
@@ -490,7 +579,6 @@ def secondary_rows(dev, stream, reps=5):
     numels = [s.numel for s in specs]
     b = api.rar_bucket_plan(numels, api.F32, wl.bucket_bytes)
     nbk, mx = api.rar_bucket_count(b)
-    bucket_bufs = [torch.empty(mx, dtype=torch.float32, device=dev) for _ in range(wl.N)]
     total = sum(numels)
     nb = alg_bytes(wl.N, total, 4, False)
     bucket_leg = oracle_timer("buckets_f32", [a[:3 * 6_250_000] for (a, _) in ranks], None, None,
@@ -499,10 +587,12 @@ def secondary_rows(dev, stream, reps=5):
     add(f"{wl.name}_tensor_lists_direct", nb,
         lambda: api.rar_bucket_allreduce_mean(b, tensors, None, api.BALANCED, api.FUSED, stream),
         None, {"buckets": nbk, **lay}, bucket_leg)
-    # ring steps per bucket: pack into bucket buffers, 2(N-1) steps, unpack
-    moved_ring = 2 * (2 * wl.N * total * 4) + 5 * (wl.N - 1) * total * 4
-    add(f"{wl.name}_pack_ring_unpack", nb,
-        lambda: api.rar_bucket_allreduce_mean(b, tensors, bucket_bufs, api.BALANCED, api.RING, stream),
+    # the 2(N-1) ring steps straight on the same pieces, every bucket's pieces
+    # in each step's launches (no packing): 3 reads+writes per element and
+    # step of the scatter-reduce, 2 of the all-gather
+    moved_ring = 5 * (wl.N - 1) * total * 4
+    add(f"{wl.name}_tensor_lists_ring", nb,
+        lambda: api.rar_bucket_allreduce_mean(b, tensors, None, api.BALANCED, api.RING, stream),
         moved_ring, {"buckets": nbk, "algo": "ring", **lay}, bucket_leg)
     # zero-copy: the tensors are views of one flat arena per rank, in backward
     # order, so bucket k is a slice of every arena and needs no packing
@@ -529,54 +619,76 @@ def secondary_rows(dev, stream, reps=5):
     add(f"{wl.name}_zero_copy_arena_separate_allocations", nb,
         lambda: api.rar_bucket_allreduce_arena(b, sep, None, api.BALANCED, api.FUSED, stream),
         None, {"buckets": nbk, "rank_layout": "separate allocations"})
-    del sep, sep_ranks, tensors, bucket_bufs
+    del sep, sep_ranks, tensors
     torch.cuda.empty_cache()
-    rows.append(overlap_row(wl, b, infos, arenas, dev, stream, nb))
-    log(f"row {rows[-1]['row']}: {rows[-1]}")
+    for r in overlap_rows(wl, b, infos, arenas, dev, stream, nb):
+        rows.append(r)
+        log(f"row {r['row']}: {r}")
     return rows
 
 
-def overlap_row(wl, b, infos, arenas, dev, stream, nb, reps=3):
+def _cu_masked_stream(cus):
+    """A HIP stream (default priority) whose kernels run only on the listed
+    compute units, wrapped for torch."""
+    import ctypes
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    ncu = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    words = (ncu + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for c in cus:
+        mask[c // 32] |= 1 << (c % 32)
+    h = ctypes.c_void_p()
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), words, mask)
+    if rc != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask: {rc}")
+    return torch.cuda.ExternalStream(h.value), h.value
+
+
+def overlap_rows(wl, b, infos, arenas, dev, stream, nb, reps=3, reserved=(32, 64)):
     """Buckets reduced while a simulated backward pass produces them.
 
-    The producer stream, for each bucket in backward order, runs a bf16
-    matrix product (4096^3, standing in for that bucket's backward compute)
-    and then copies the bucket's gradients into every rank's arena, and
-    records the bucket's ready event; the reduction stream waits for each
-    event in turn (rar_bucket_allreduce_arena).  Reported: producer alone,
-    reduction alone, both together, and the fraction of the reduction time
-    hidden behind the producer."""
+    The producer stream works through the buckets in backward order: a bf16
+    matrix product (4096^3, standing in for that bucket's backward compute),
+    then one write of the bucket's gradients into every rank's arena (a fill:
+    each gradient byte written once, nothing read), then the bucket's ready
+    event.  The reduction stream waits for each event in turn
+    (rar_bucket_allreduce_arena).  Each row gives the producer alone, the
+    reduction alone, both together on the same streams, and the fraction of
+    the reduction time hidden.  The first row uses ordinary streams (the
+    whole chip for each); the others reserve K compute units for the
+    reduction and give the producer the rest, and also compare the overlapped
+    time with the producer and reduction run back to back on the whole chip."""
+    import ctypes
     import torch
     from ring_all_reduce_amd import api
     N = len(arenas)
-    pristine = [a.clone() for a in arenas]
     x = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
-    producer, comm = torch.cuda.Stream(), torch.cuda.Stream()
+    gemm_flops = 2 * 4096 ** 3 * len(infos)
+    prod_bytes = sum(el for (_, el, _) in infos) * 4 * N
 
-    def produce(events):
+    def produce(producer, events):
         with torch.cuda.stream(producer):
-            y = x
             for k, (so, el, _) in enumerate(infos):
-                y = torch.matmul(x, x)
+                torch.matmul(x, x)
                 for n in range(N):
-                    arenas[n][so:so + el].copy_(pristine[n][so:so + el])
+                    arenas[n][so:so + el].fill_(1e-3 * (k + 1) * (n + 1))
                 if events is not None:
                     events[k].record(producer)
-        return y
 
-    def timed(run_prod, run_comm):
+    def timed(producer, comm, run_prod, run_comm):
         best = None
         for _ in range(reps):
             events = [torch.cuda.Event() for _ in infos] if (run_prod and run_comm) else None
             torch.cuda.synchronize()
-            t0 = torch.cuda.Event(enable_timing=True)
-            tp = torch.cuda.Event(enable_timing=True)
-            tc = torch.cuda.Event(enable_timing=True)
+            t0, tp, tc = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             t0.record(stream)
             producer.wait_event(t0)
             comm.wait_event(t0)
             if run_prod:
-                produce(events)
+                produce(producer, events)
             tp.record(producer)
             if run_comm:
                 api.rar_bucket_allreduce_arena(b, arenas, events, stream=comm)
@@ -586,15 +698,39 @@ def overlap_row(wl, b, infos, arenas, dev, stream, nb, reps=3):
             best = ms if best is None else min(best, ms)
         return best
 
-    t_prod = timed(True, False)
-    t_comm = timed(False, True)
-    t_both = timed(True, True)
-    hidden = (t_prod + t_comm - t_both) / t_comm if t_comm > 0 else 0.0
-    return {"row": f"{wl.name}_overlap_simulated_backward", "buckets": len(infos),
-            "producer_ms": round(t_prod, 3), "allreduce_ms": round(t_comm, 3), "overlapped_ms": round(t_both, 3),
-            "allreduce_alg_GBps": round(nb / (t_comm * 1e-3) / 1e9, 1),
-            "fraction_of_allreduce_hidden": round(hidden, 3),
-            "producer": "per bucket: bf16 4096^3 matmul + copy of the bucket into every arena"}
+    def row(name, producer, comm, extra):
+        t_prod = timed(producer, comm, True, False)
+        t_comm = timed(producer, comm, False, True)
+        t_both = timed(producer, comm, True, True)
+        r = {"row": name, "buckets": len(infos), "producer_ms": round(t_prod, 3), "allreduce_ms": round(t_comm, 3),
+             "overlapped_ms": round(t_both, 3), "allreduce_alg_GBps": round(nb / (t_comm * 1e-3) / 1e9, 1),
+             "fraction_of_allreduce_hidden": round((t_prod + t_comm - t_both) / t_comm, 3),
+             "producer": (f"per bucket: bf16 4096^3 matmul, then one fill of the bucket in every arena "
+                          f"({gemm_flops / 1e12:.1f} TFLOP and {prod_bytes / 1e9:.2f} GB written in all)")}
+        r.update(extra)
+        return r
+
+    rows = [row(f"{wl.name}_overlap_simulated_backward", torch.cuda.Stream(), torch.cuda.Stream(),
+                {"streams": "ordinary (every CU for each)"})]
+    full_prod, full_comm = rows[0]["producer_ms"], rows[0]["allreduce_ms"]
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    for k in reserved:
+        comm, hc = _cu_masked_stream(range(k))
+        producer, hp = _cu_masked_stream(range(k, ncu))
+        try:
+            r = row(f"{wl.name}_overlap_simulated_backward_reduction_on_{k}_cus", producer, comm,
+                    {"streams": f"reduction on CUs 0-{k - 1}, producer on CUs {k}-{ncu - 1} "
+                                "(hipExtStreamCreateWithCUMask)",
+                     "back_to_back_full_chip_ms": round(full_prod + full_comm, 3)})
+            r["vs_back_to_back_full_chip"] = round((full_prod + full_comm) / r["overlapped_ms"], 3)
+            rows.append(r)
+        finally:
+            torch.cuda.synchronize()
+            hip.hipStreamDestroy(hc)
+            hip.hipStreamDestroy(hp)
+    return rows
 
 
 def oracle_timer(kind, bufs, w, lr, sample_elems=20_000_000, bucket_elems=None, one_thread=False):

@@ -144,7 +144,12 @@ rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *stride_bytes);
  * (N-1) * stride + P * element size <= pool_bytes, and returns the fastest
  * in *stride_bytes (each candidate: one untimed and two timed calls in each
  * of four rounds, forward and backward in turn; the smallest median of the
- * eight wins, ties to the smaller stride).  The pool's contents are
+ * eight wins, ties to the smaller stride -- except that the stride
+ * rar_rank_stride gives, when it is a candidate, is kept if its median lies
+ * within the winner's by no more than the larger of the two candidates'
+ * spreads, the range of the middle six of their eight timings: on MI355X the
+ * fast strides lie within about 1% of each other, about as much as single
+ * calls vary).  The pool's contents are
  * overwritten; the call enqueues on `stream` and waits for it, so it must
  * not run under graph capture.  N == 1 or P == 0 returns s0
  * without device work.  Which strides are fast differs by shape (see
@@ -156,6 +161,16 @@ rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *stride_bytes);
  * RAR_EHIP / RAR_ENOMEM: a HIP call failed. */
 rar_status rar_rank_stride_tune(int N, int64_t P, rar_dtype dtype, void *pool, int64_t pool_bytes,
                                 int max_candidates, void *stream, int64_t *stride_bytes);
+
+/* rar_rank_stride_tune, also reporting what it measured: *n_candidates
+ * receives K, the number of candidates timed (0 when N == 1 or P == 0), and
+ * for k < K cand_stride[k], median_ms[k] and spread_ms[k] (the range of the
+ * middle six of candidate k's eight timings).  The arrays hold
+ * max_candidates entries; any of these outputs may be NULL. */
+rar_status rar_rank_stride_tune_stats(int N, int64_t P, rar_dtype dtype, void *pool, int64_t pool_bytes,
+                                      int max_candidates, void *stream, int64_t *stride_bytes,
+                                      int *n_candidates, int64_t cand_stride[], float median_ms[],
+                                      float spread_ms[]);
 
 /* Free the plan and its workspace (if any).  Waits for the device to finish
  * work that may use the workspace.  NULL is accepted. */
@@ -285,6 +300,11 @@ rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void *const buc
  * per bucket) and bucket_bufs may be NULL.
  * The jobs of consecutive buckets then share launches, so all N*n_tensors
  * tensors must be pairwise disjoint memory (RAR_EINVAL otherwise).
+ * With RAR_ALGO_RING, RAR_F32 and N >= 2 the 2(N-1) ring steps of
+ * [Gibiansky] §Scatter-reduce and §Allgather run on those same pieces in
+ * place (5*(N-1)*size*4 bytes moved per bucket, no packing); each step is
+ * a few launches over the pieces of every bucket, so the tensors must again
+ * be pairwise disjoint, and bucket_bufs may be NULL.
  * Otherwise each bucket is packed into bucket_bufs[n] (N device buffers of at
  * least max_bucket_elems elements, 16-byte aligned, reused by every bucket,
  * overlapping neither each other nor the tensors: RAR_EINVAL), reduced with
@@ -305,9 +325,10 @@ rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunki
  * does not block the host.  Every bucket start must be 16-byte aligned
  * (RAR_EALIGN otherwise; a bucket size that is a multiple of 16 bytes gives
  * that), and the N arenas (total elements each) must not overlap
- * (RAR_EINVAL).  With RAR_ALGO_FUSED and N in {2, 4, 8, 10, 16, 40} the
- * buckets between two ready events share launches.  Results are
- * bit-identical to rar_allreduce_mean on each slice. */
+ * (RAR_EINVAL).  With RAR_ALGO_FUSED and N in {2, 4, 8, 10, 16, 40}, and
+ * with RAR_ALGO_RING, RAR_F32 and N >= 2 (ring steps over every chunk of those
+ * buckets at once), the buckets between two ready events share launches.
+ * Results are bit-identical to rar_allreduce_mean on each slice. */
 rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
                                       void *const arenas[], void *const ready_events[], void *stream);
 
@@ -318,7 +339,7 @@ const char *rar_strerror(rar_status s);
 
 /* Library version as major*10000 + minor*100 + patch (0.2.0 = 200 adds
  * rar_rank_stride, 0.3.0 = 300 rar_rank_stride_tune, 0.4.0 = 400
- * rar_allreduce_ring_noalloc). */
+ * rar_allreduce_ring_noalloc, 0.5.0 = 500 rar_rank_stride_tune_stats). */
 int rar_version(void);
 
 #ifdef __cplusplus

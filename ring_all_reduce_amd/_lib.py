@@ -22,6 +22,8 @@ SIGNATURES = {
     "rar_plan_destroy": (_int, [_vp]),
     "rar_rank_stride": (_int, [_i64, _int, _i64p]),
     "rar_rank_stride_tune": (_int, [_int, _i64, _int, _vp, _i64, _int, _vp, _i64p]),
+    "rar_rank_stride_tune_stats": (_int, [_int, _i64, _int, _vp, _i64, _int, _vp, _i64p, _ip, _i64p,
+                                          ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
     "rar_plan_set_algo": (_int, [_vp, _int]),
     "rar_plan_set_grid": (_int, [_vp, _int]),
     "rar_plan_chunk": (_int, [_vp, _int, _i64p, _i64p, _ip]),

@@ -154,6 +154,21 @@ def rar_rank_stride_tune(N: int, P: int, dtype: int, pool, candidates: int = 12,
     return out.value
 
 
+def rar_rank_stride_tune_stats(N: int, P: int, dtype: int, pool, candidates: int = 12, stream=None):
+    """rar_rank_stride_tune and its measurements: (stride, [(candidate stride,
+    median ms, spread ms), ...])."""
+    if not hasattr(pool, "element_size"):
+        raise TypeError("pool must be a tensor (its size bounds the candidates)")
+    nbytes = pool.numel() * pool.element_size()
+    out, K = ctypes.c_int64(), ctypes.c_int()
+    cs = (ctypes.c_int64 * candidates)()
+    med, spr = (ctypes.c_float * candidates)(), (ctypes.c_float * candidates)()
+    _check(lib().rar_rank_stride_tune_stats(int(N), int(P), int(dtype), _addr(pool), int(nbytes), int(candidates),
+                                            _stream(stream), ctypes.byref(out), ctypes.byref(K), cs, med, spr),
+           "rar_rank_stride_tune_stats")
+    return out.value, [(cs[k], med[k], spr[k]) for k in range(K.value)]
+
+
 def rar_plan_destroy(plan: Plan) -> None:
     if plan.handle:
         h, plan.handle = plan.handle, ctypes.c_void_p()

@@ -21,6 +21,9 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "librar.so"
 SOURCES = [CSRC / "rar_host.cpp", CSRC / "rar_kernels.hip"]
+# reference stream kernels for the benchmark's ceiling rows (not the path)
+REF_LIB = PKG / "libstream_ref.so"
+REF_SOURCES = [CSRC / "stream_ref.hip"]
 
 ARCH = os.environ.get("RAR_OFFLOAD_ARCH", "gfx950")
 
@@ -40,9 +43,15 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra=()) -> pathlib.Path:
-    """Compile every source into librar.so; always rebuilds."""
-    tmp = LIB.with_suffix(".so.tmp%d" % os.getpid())
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, *map(str, SOURCES), "-o", str(tmp)]
+    """Compile librar.so and the benchmark's libstream_ref.so; always rebuilds."""
+    _build_one(SOURCES, LIB, verbose, extra)
+    _build_one(REF_SOURCES, REF_LIB, verbose, extra)
+    return LIB
+
+
+def _build_one(sources, lib, verbose, extra) -> None:
+    tmp = lib.with_suffix(".so.tmp%d" % os.getpid())
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, *map(str, sources), "-o", str(tmp)]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,8 +62,7 @@ def build(verbose: bool = False, extra=()) -> pathlib.Path:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
     if verbose and msg.strip():
         print(msg, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

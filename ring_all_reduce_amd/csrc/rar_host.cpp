@@ -290,6 +290,15 @@ extern "C" rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *strid
 extern "C" rar_status rar_rank_stride_tune(int N, int64_t P, rar_dtype dtype, void *pool, int64_t pool_bytes,
                                            int max_candidates, void *stream, int64_t *stride_bytes)
 {
+    return rar_rank_stride_tune_stats(N, P, dtype, pool, pool_bytes, max_candidates, stream, stride_bytes, nullptr,
+                                      nullptr, nullptr, nullptr);
+}
+
+extern "C" rar_status rar_rank_stride_tune_stats(int N, int64_t P, rar_dtype dtype, void *pool, int64_t pool_bytes,
+                                                 int max_candidates, void *stream, int64_t *stride_bytes,
+                                                 int *n_candidates, int64_t cand_stride[], float median_ms[],
+                                                 float spread_ms[])
+{
     constexpr int64_t MiB = int64_t(1) << 20;
     if (!stride_bytes || N < 1 || N > kMaxRanks || P < 0 || !valid_dtype(dtype) || max_candidates < 1 ||
         max_candidates > kMaxStrideCandidates || pool_bytes < 0 || P > (INT64_MAX / 4) / elem_bytes(dtype))
@@ -297,6 +306,8 @@ extern "C" rar_status rar_rank_stride_tune(int N, int64_t P, rar_dtype dtype, vo
     const int64_t need = P * elem_bytes(dtype);
     // candidates: the multiples of 2 MiB from the smallest one >= need
     const int64_t s0 = std::max<int64_t>(2 * MiB, (need + 2 * MiB - 1) / (2 * MiB) * (2 * MiB));
+    if (n_candidates)
+        *n_candidates = 0;
     if (N == 1 || P == 0) {  // nothing to place relative to anything
         *stride_bytes = s0;
         return RAR_OK;
@@ -351,21 +362,39 @@ extern "C" rar_status rar_rank_stride_tune(int N, int64_t P, rar_dtype dtype, vo
             }
         }
     if (rc == RAR_OK) {
-        // the smallest median of the eight timings (the mean of the middle
-        // two); ties go to the smaller stride
+        // per candidate: the median of the eight timings (the mean of the
+        // middle two) and their spread (the range of the middle six).  The
+        // smallest median wins (ties to the smaller stride) -- unless the
+        // static rule's stride (rar_rank_stride) is a candidate and lies
+        // within the larger of the two spreads of the winner, in which case
+        // the measurement cannot tell them apart and the static stride stays.
         constexpr int kSamples = kRounds * kTimed;
+        float med[kMaxStrideCandidates], spread[kMaxStrideCandidates];
         int best = 0;
-        float best_ms = 0.0f;
         for (int k = 0; k < K; ++k) {
             float *t = ms[k];
             std::sort(t, t + kSamples);
-            const float med = 0.5f * (t[kSamples / 2 - 1] + t[kSamples / 2]);
-            if (k == 0 || med < best_ms) {
+            med[k] = 0.5f * (t[kSamples / 2 - 1] + t[kSamples / 2]);
+            spread[k] = t[kSamples - 2] - t[1];
+            if (med[k] < med[best])
                 best = k;
-                best_ms = med;
-            }
         }
+        int64_t fixed = 0;
+        (void)rar_rank_stride(P, dtype, &fixed);
+        const int64_t si = (fixed - s0) / (2 * MiB);
+        if (si >= 0 && si < K && si != best && med[si] - med[best] <= std::max(spread[si], spread[best]))
+            best = (int)si;
         *stride_bytes = s0 + 2 * MiB * best;
+        if (n_candidates)
+            *n_candidates = K;
+        for (int k = 0; k < K; ++k) {
+            if (cand_stride)
+                cand_stride[k] = s0 + 2 * MiB * k;
+            if (median_ms)
+                median_ms[k] = med[k];
+            if (spread_ms)
+                spread_ms[k] = spread[k];
+        }
     }
     for (hipEvent_t e : ev)
         if (e)
@@ -908,12 +937,14 @@ rar_status bucket_plans(rar_buckets_t b, int N, rar_chunking chunking, rar_algo 
 
 namespace {
 
-// Bucket k reduced in place in the tensors: each segment is cut at the
+// Bucket k cut into pieces in the tensors: each segment is cut at the
 // bucket's chunk boundaries into pieces with a uniform fold start.  A piece
 // that continues the previous one (same chunk, and in every rank it starts
 // where the previous one ends: tensors that are views of one flat buffer)
-// extends it, so such tensors give the jobs of one flat arena.
-rar_status bucket_direct(rar_buckets_t b, int k, int N, const rar_plan_s *pl, void *const tensors[], JobBatch &jb)
+// extends it, so such tensors give the pieces of one flat arena.  Each piece
+// goes to sink.add(len, c, first) (first[n]: rank n's first element).
+template <class Sink>
+rar_status bucket_pieces(rar_buckets_t b, int k, int N, const rar_plan_s *pl, void *const tensors[], Sink &jb)
 {
     const int es = elem_bytes(b->dtype);
     char *first[kMaxRanks], *next[kMaxRanks];
@@ -948,6 +979,107 @@ rar_status bucket_direct(rar_buckets_t b, int k, int N, const rar_plan_s *pl, vo
     return len > 0 ? jb.add(len, c_pending, first) : RAR_OK;
 }
 
+// The ring steps of [Gibiansky] §Scatter-reduce and §Allgather run straight
+// on bucket pieces (binary32): at scatter-reduce step s the piece of chunk c
+// moves from rank (c+s) mod N to rank (c+s+1) mod N and is added there (the
+// last step, at the owner, divides by N); at all-gather step s it moves from
+// rank (c+s-1) mod N to rank (c+s) mod N and overwrites.  Pieces are
+// gathered until flush(); then each step is one or a few launches over all
+// of them (jobs under 1 MiB in launches of their own, so their grid rows are
+// not padded to full chunks).  Pieces of different buckets are disjoint
+// memory, so sharing launches changes no result.
+struct RingPieces {
+    int N;
+    hipStream_t st;
+    std::vector<int64_t> len;
+    std::vector<int> chunk;
+    std::vector<char *> ptr;  // piece i, rank n: ptr[i*N + n]
+
+    RingPieces(int N_, hipStream_t st_) : N(N_), st(st_) {}
+
+    rar_status add(int64_t n, int c, char *const first[])
+    {
+        if (n <= 0)
+            return RAR_OK;
+        len.push_back(n);
+        chunk.push_back(c);
+        ptr.insert(ptr.end(), first, first + N);
+        return RAR_OK;
+    }
+
+    static bool small(int64_t n) { return n * 4 < JobBatch::kSmallBytes; }
+
+    rar_status scatter_reduce_step(int s, bool last)
+    {
+        for (int pass = 0; pass < 2; ++pass) {  // big pieces, then small ones
+            rar::StepJobsParams jp{};
+            jp.N = N;
+            int64_t mx = 0;
+            for (size_t i = 0; i < len.size(); ++i) {
+                if (small(len[i]) != (pass == 1))
+                    continue;
+                const int c = chunk[i];
+                jp.job[jp.njobs++] = {reinterpret_cast<const float *>(ptr[i * N + (c + s) % N]),
+                                      reinterpret_cast<float *>(ptr[i * N + (c + s + 1) % N]), len[i]};
+                mx = std::max(mx, len[i]);
+                if (jp.njobs == rar::kMaxStepJobs) {
+                    hipError_t e = rar::launch_sr_jobs(jp, last, mx, st);
+                    if (e != hipSuccess)
+                        return RAR_EHIP;
+                    jp.njobs = 0;
+                    mx = 0;
+                }
+            }
+            if (jp.njobs && rar::launch_sr_jobs(jp, last, mx, st) != hipSuccess)
+                return RAR_EHIP;
+        }
+        return RAR_OK;
+    }
+
+    rar_status allgather_step(int s)
+    {
+        for (int pass = 0; pass < 2; ++pass) {
+            rar::CopyParams cp{};
+            cp.unit = 4;
+            int64_t mx = 0;
+            for (size_t i = 0; i < len.size(); ++i) {
+                if (small(len[i]) != (pass == 1))
+                    continue;
+                const int c = chunk[i];
+                cp.job[cp.njobs++] = {ptr[i * N + (c + s - 1 + N) % N], ptr[i * N + (c + s) % N], len[i] * 4};
+                mx = std::max(mx, len[i] * 4);
+                if (cp.njobs == rar::kMaxCopyJobs) {
+                    if (rar::launch_copy(cp, kDefaultBlocks, mx, st) != hipSuccess)
+                        return RAR_EHIP;
+                    cp.njobs = 0;
+                    mx = 0;
+                }
+            }
+            if (cp.njobs && rar::launch_copy(cp, kDefaultBlocks, mx, st) != hipSuccess)
+                return RAR_EHIP;
+        }
+        return RAR_OK;
+    }
+
+    rar_status flush()
+    {
+        rar_status rc = RAR_OK;
+        for (int s = 0; s < N - 1 && rc == RAR_OK; ++s)
+            rc = scatter_reduce_step(s, s == N - 2);
+        for (int s = 0; s < N - 1 && rc == RAR_OK; ++s)
+            rc = allgather_step(s);
+        len.clear();
+        chunk.clear();
+        ptr.clear();
+        return rc;
+    }
+};
+
+// Buckets whose ring steps run on their pieces in place: binary32 at N >= 2
+// (bf16 keeps its partial sums in a plan's workspace and goes through bucket
+// buffers; one rank has no transfers).
+bool ring_on_pieces(rar_dtype dt, int N, rar_algo algo) { return algo == RAR_ALGO_RING && dt == RAR_F32 && N >= 2; }
+
 }  // namespace
 
 extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
@@ -957,7 +1089,8 @@ extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chun
         if (!b || !valid_bucket_call(N, chunking, algo))
             return RAR_EINVAL;
         const int nb = (int)b->segs.size();
-        const bool direct = algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N);
+        const bool ring_direct = ring_on_pieces(b->dtype, N, algo);
+        const bool direct = (algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N)) || ring_direct;
         for (int k = 0; k < nb; ++k) {
             rar_status rc = check_bucket_args(b, k, N, tensors, bucket_bufs, !direct);
             if (rc != RAR_OK)
@@ -972,9 +1105,15 @@ extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chun
             rc = check_tensors_disjoint(b, N, tensors);
             if (rc != RAR_OK)
                 return rc;
+            if (ring_direct) {
+                RingPieces rp(N, st);
+                for (int k = 0; k < nb && rc == RAR_OK; ++k)
+                    rc = bucket_pieces(b, k, N, plan_of[k], tensors, rp);
+                return rc != RAR_OK ? rc : rp.flush();
+            }
             JobBatch jb(b->dtype, N, st);
             for (int k = 0; k < nb; ++k) {
-                rc = bucket_direct(b, k, N, plan_of[k], tensors, jb);
+                rc = bucket_pieces(b, k, N, plan_of[k], tensors, jb);
                 if (rc != RAR_OK)
                     return rc;
             }
@@ -1045,6 +1184,28 @@ extern "C" rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chu
             }
             return jb.flush();
         }
+        if (ring_on_pieces(b->dtype, N, algo)) {
+            // the buckets between two ready events run their ring steps together
+            RingPieces rp(N, st);
+            char *first[kMaxRanks];
+            for (int k = 0; k < nb; ++k) {
+                if (ready_events && ready_events[k]) {
+                    rc = rp.flush();
+                    if (rc != RAR_OK)
+                        return rc;
+                    const hipError_t e = hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0);
+                    if (e != hipSuccess)
+                        return hip_failed(e);
+                }
+                const rar_plan_s *pl = plan_of[k];
+                for (int c = 0; c < N; ++c) {
+                    for (int n = 0; n < N; ++n)
+                        first[n] = static_cast<char *>(arenas[n]) + (b->start[k] + pl->ct.off[c]) * es;
+                    rp.add(pl->ct.off[c + 1] - pl->ct.off[c], c, first);
+                }
+            }
+            return rp.flush();
+        }
         void *slice[kMaxRanks];
         for (int k = 0; k < nb; ++k) {
             if (ready_events && ready_events[k]) {
@@ -1078,4 +1239,4 @@ extern "C" const char *rar_strerror(rar_status s)
     return "unknown status";
 }
 
-extern "C" int rar_version(void) { return 400; }  // 0.4.0: rar_allreduce_ring_noalloc added
+extern "C" int rar_version(void) { return 500; }  // 0.5.0: rar_rank_stride_tune_stats added

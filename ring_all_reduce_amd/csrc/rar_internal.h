@@ -11,7 +11,7 @@ namespace rar {
 
 constexpr int kMaxRanks = RAR_MAX_RANKS;
 constexpr int kThreads = 256;   // workgroup size of every kernel: four 64-wide waves
-constexpr int kMaxCopyJobs = 64;
+constexpr int kMaxCopyJobs = 128;
 
 // Chunk table: chunk c is [off[c], off[c+1]).  Passed to kernels by value in the
 // kernel-argument segment, so a wave-uniform index becomes a scalar load.
@@ -75,6 +75,23 @@ struct JobsParams {
     int njobs;
 };
 
+// Ring steps straight on bucket pieces: one transfer per piece per step, the
+// receiver's piece += the sender's (binary32), divided by N on the last
+// scatter-reduce step.
+struct StepJob {
+    const float *src;
+    float *dst;
+    int64_t len;  // elements
+};
+
+constexpr int kMaxStepJobs = 128;
+
+struct StepJobsParams {
+    StepJob job[kMaxStepJobs];
+    int njobs;
+    int N;
+};
+
 // Single reducer (prior art): rank 0 accumulates rank `src`.
 struct PairParams {
     RankPtrs bufs;
@@ -92,6 +109,7 @@ hipError_t launch_sr_step(rar_dtype dt, const StepParams &p, bool first, bool la
                           int max_blocks, int64_t max_chunk, hipStream_t st);
 hipError_t launch_copy(const CopyParams &p, int max_blocks, int64_t max_job_bytes, hipStream_t st);
 hipError_t launch_pair_add(const PairParams &p, bool last, bool sgd, int max_blocks, hipStream_t st);
+hipError_t launch_sr_jobs(const StepJobsParams &p, bool last, int64_t max_len, hipStream_t st);
 // The binary32 workspace held in the library's static device array: its
 // address on `device`, which must be the current device (looked up on the
 // first call for that device, then kept).

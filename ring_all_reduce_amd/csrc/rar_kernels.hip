@@ -861,6 +861,65 @@ __global__ __launch_bounds__(kThreads) void rar_sr_step_bf16(StepParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Scatter-reduce step over a table of pieces (buckets straight from the
+// tensors): job j adds the sender's piece into the receiver's, elementwise;
+// on the last step the receiver is the piece's owner and divides by N.  The
+// pieces of one step are disjoint and none is both read and written in it
+// ([Gibiansky] §Scatter-reduce, per chunk of each bucket), so one launch
+// carries any number of them.
+// ---------------------------------------------------------------------------
+
+template <bool LAST>
+__global__ __launch_bounds__(kThreads) void rar_sr_jobs_f32(StepJobsParams p)
+{
+    const StepJob jb = p.job[blockIdx.y];
+    const float *sp = jb.src;
+    float *dp = jb.dst;
+    const int64_t n = jb.len;
+    const float fN = (float)p.N;
+    auto elem = [&](int64_t e) {
+        float v = dp[e] + sp[e];
+        if (LAST)
+            v = v / fN;
+        dp[e] = v;
+    };
+    if ((((uintptr_t)sp ^ (uintptr_t)dp) & 15) != 0) {
+        // the two ranks' pieces differ in their 16-byte alignment
+        for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (int64_t)gridDim.x * kThreads)
+            elem(e);
+        return;
+    }
+    // scalar elements up to the receiver's first 128-byte line (so no line is
+    // written by two workgroups) and after the last whole 16-byte group
+    int64_t h = (int64_t)(((128 - ((uintptr_t)dp & 127)) & 127) / 4);
+    if (h > n)
+        h = n;
+    const int64_t nvec = (n - h) / 4;
+    const int64_t tail0 = h + nvec * 4;
+    if (blockIdx.x == 0) {
+        const int t = threadIdx.x;
+        if (t < 32) {
+            if (t < h)
+                elem(t);
+        } else if (t - 32 < n - tail0) {
+            elem(tail0 + (t - 32));
+        }
+    }
+    const f32x4 *s4 = reinterpret_cast<const f32x4 *>(sp + h);
+    f32x4 *d4 = reinterpret_cast<f32x4 *>(dp + h);
+    const int64_t ntiles = (nvec + kThreads - 1) / kThreads;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t v = t * kThreads + threadIdx.x;
+        if (v < nvec) {
+            f32x4 x = ld(d4 + v) + ld(s4 + v);
+            if (LAST)
+                x = x / fN;
+            st(d4 + v, x);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Multi-job copy: all-gather steps ([Gibiansky] §Allgather: the receiver
 // overwrites), bucket pack/unpack, and the single reducer's broadcast.
 // ---------------------------------------------------------------------------
@@ -1166,6 +1225,18 @@ hipError_t launch_sr_step(rar_dtype dt, const StepParams &p, bool first, bool la
     } else {
         hipLaunchKernelGGL((rar_sr_step_bf16<false, false, false>), g, b, 0, st, p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_sr_jobs(const StepJobsParams &p, bool last, int64_t max_len, hipStream_t st)
+{
+    if (p.njobs <= 0)
+        return hipSuccess;
+    const dim3 g(blocks_x(1 << 24, p.njobs, max_len / 4 + 1, 1), p.njobs);
+    if (last)
+        hipLaunchKernelGGL((rar_sr_jobs_f32<true>), g, dim3(kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((rar_sr_jobs_f32<false>), g, dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 

@@ -576,7 +576,8 @@ def test_sixty_four_ranks_sampled(dt):
 # Buckets reduced as a simulated backward pass produces them
 # ---------------------------------------------------------------------------
 
-def test_bucket_arena_waits_for_each_ready_event():
+@pytest.mark.parametrize("algo", [api.FUSED, api.RING])
+def test_bucket_arena_waits_for_each_ready_event(algo):
     # The producer stream writes bucket k only after a long matrix product, the
     # arenas start as NaN, and the reduction runs on another stream: a reduction
     # that did not wait for bucket k's event would read NaN and fail parity.
@@ -603,7 +604,7 @@ def test_bucket_arena_waits_for_each_ready_event():
             e = torch.cuda.Event()
             e.record(producer)
             events.append(e)
-    api.rar_bucket_allreduce_arena(b, arenas, events, stream=comm)
+    api.rar_bucket_allreduce_arena(b, arenas, events, algo=algo, stream=comm)
     comm.synchronize()
     producer.synchronize()
     for n in range(1, N):
@@ -638,6 +639,12 @@ def test_bucket_arena_without_events_matches_pack_path():
         torch.cuda.synchronize()
         for n in range(N):
             assert torch.equal(ar[n], flat[n])
+        got = ar[0].cpu().numpy()
+        for k in range(api.rar_bucket_count(b)[0]):
+            so, el, _ = api.rar_bucket_info(b, k)
+            part = [np.ascontiguousarray(h[so:so + el]) for h in host]
+            oracle.ring_allreduce_f32(part, oracle.partition(N, el))
+            _assert_bits(got[so:so + el], part[0], f"algo {algo} bucket {k}")
 
 
 @pytest.mark.parametrize("algo", [api.FUSED, api.RING])
@@ -666,9 +673,10 @@ def test_bucketed_bf16_small_transformer_bit_exact(algo):
             assert got.tobytes() == part[n].tobytes(), f"rank {n}: first diff {_first_diff(got, part[n])}"
 
 
+@pytest.mark.parametrize("algo", [api.FUSED, api.RING])
 @pytest.mark.parametrize("skew", ["same", "different"])
 @pytest.mark.parametrize("dt", [api.F32, api.BF16])
-def test_bucket_tensors_direct_with_misaligned_views(skew, dt):
+def test_bucket_tensors_direct_with_misaligned_views(skew, dt, algo):
     # Tensors are views at odd element offsets: with the same offset on every
     # rank the direct path runs vector bodies with scalar heads and tails; with
     # different offsets per rank it runs the scalar path.  Both must match the
@@ -697,7 +705,10 @@ def test_bucket_tensors_direct_with_misaligned_views(skew, dt):
             pos += k
         tensors.append(ts)
     b = api.rar_bucket_plan(numels, dt, bucket_bytes)
-    api.rar_bucket_allreduce_mean(b, tensors, None)
+    # binary32 ring steps run on the tensor pieces directly; bf16 ring steps pack
+    bufs = [torch.empty(api.rar_bucket_count(b)[1], dtype=tdt, device=DEV) for _ in range(N)] \
+        if algo == api.RING else None
+    api.rar_bucket_allreduce_mean(b, tensors, bufs, api.BALANCED, algo)
     torch.cuda.synchronize()
     layout = oracle.bucket_layout(numels, es, bucket_bytes)
     stream = [h.copy() for h in host]
@@ -1293,6 +1304,20 @@ def test_rank_stride_tune_picks_a_fitting_candidate_and_stays_exact(key):
     pool = torch.zeros(synth.pool_elements(wl, cands[-1], P, N), dtype=tdt, device=DEV)
     stride = api.rar_rank_stride_tune(N, P, dt, pool, candidates=K)
     assert stride in cands
+    # the measurements behind a pick: the smallest median wins unless the
+    # static rule's stride is within the larger of the two spreads
+    pick, stats = api.rar_rank_stride_tune_stats(N, P, dt, pool, candidates=K)
+    assert [c for c, _, _ in stats] == cands and pick in cands
+    assert all(m > 0 and sp >= 0 for _, m, sp in stats)
+    med = {c: m for c, m, _ in stats}
+    spread = {c: sp for c, _, sp in stats}
+    best = min(cands, key=lambda c: (med[c], c))
+    static = api.rar_rank_stride(P, dt)
+    f = np.float32  # the library compares in binary32
+    if static in med and f(f(med[static]) - f(med[best])) <= max(f(spread[static]), f(spread[best])):
+        assert pick == static
+    else:
+        assert pick == best
     # more candidates asked for than fit: only those that fit are tried
     assert api.rar_rank_stride_tune(N, P, dt, pool, candidates=K + 20) in cands
     # a pool that holds only the first candidate, and one element less
