@@ -114,10 +114,10 @@ def layout_note(stride, P, dt, full=False):
     return note
 
 
-def committed_traffic(workload_name: str):
+def committed_traffic(workload_name: str, dtype: str = "f32"):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source; else None."""
-    f = PROFILES / f"fused_f32_sgd_{workload_name}_pmc.md"
+    f = PROFILES / f"fused_{dtype}_sgd_{workload_name}_pmc.md"
     if not f.exists():
         return None
     m = re.search(r"```json\s*(\{.*?\})\s*```", f.read_text(), re.S)
@@ -270,7 +270,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": committed_traffic(wl.name) if args.algo == "fused" else None,
+            "traffic": committed_traffic(wl.name, wl.dtype) if args.algo == "fused" else None,
             "algorithmic_bytes_per_launch": nbytes,
             "avg_launch_ms": round(kern_ms, 5),
             "median_launch_ms": round(statistics.median(per_ms), 5),
@@ -302,9 +302,10 @@ def main():
 # ---------------------------------------------------------------------------
 
 def profile_bucketed(wl, dev, stream, iters):
-    """Counter runs of the bucketed workload: per iteration, the reduction
-    straight from the tensor lists, the 1.2 GB calibration copy, and the
-    reduction over the per-rank arenas (one call each)."""
+    """Counter runs of the bucketed workload: per iteration, the fused
+    reduction straight from the tensor lists, the 1.2 GB calibration copy,
+    the fused reduction over the per-rank arenas, and the ring steps straight
+    on the tensor lists (one call each)."""
     import torch
     from ring_all_reduce_amd import api, synth
     stride, pool = tuned_pool(wl, dev, stream)  # the layout the bench rows use
@@ -318,6 +319,7 @@ def profile_bucketed(wl, dev, stream, iters):
         api.rar_bucket_allreduce_mean(b, tensors, None, api.BALANCED, api.FUSED, stream)
         cal.run_once(stream)
         api.rar_bucket_allreduce_arena(b, arenas, None, api.BALANCED, api.FUSED, stream)
+        api.rar_bucket_allreduce_mean(b, tensors, None, api.BALANCED, api.RING, stream)
     torch.cuda.synchronize()
     total = sum(sp.numel for sp in specs)
     print(json.dumps({"profile_mode": True, "workload": wl.name, "calls_per_path": iters, "rank_stride": stride,
