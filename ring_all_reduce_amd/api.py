@@ -71,9 +71,14 @@ def _ranks(xs: Sequence, N: int, what: str) -> ctypes.Array:
     return _ptr_array(xs)
 
 
+_DTYPES = {}
+
+
 def _torch_dtype(dtype: int):
-    import torch
-    return torch.float32 if dtype == F32 else torch.bfloat16
+    if dtype not in _DTYPES:
+        import torch
+        _DTYPES[dtype] = torch.float32 if dtype == F32 else torch.bfloat16
+    return _DTYPES[dtype]
 
 
 def _check_tensor(x, what: str, dtype: int, min_numel: int) -> None:
@@ -91,7 +96,8 @@ def _check_tensor(x, what: str, dtype: int, min_numel: int) -> None:
 
 def _check_ranks(xs: Sequence, what: str, dtype: int, min_numel: int) -> None:
     for n, x in enumerate(xs):
-        _check_tensor(x, f"{what}[{n}]", dtype, min_numel)
+        if hasattr(x, "data_ptr") and (x.dtype != _torch_dtype(dtype) or x.numel() < min_numel):
+            _check_tensor(x, f"{what}[{n}]", dtype, min_numel)  # raises, with the argument's name
 
 
 def _stream(s) -> int:
@@ -300,11 +306,14 @@ def rar_bucket_segment(b: Buckets, bucket: int, seg: int):
 
 def _rank_major(b: "Buckets", tensors: Sequence[Sequence]) -> ctypes.Array:
     # the library reads N * n_tensors pointers: every rank must list them all
+    want, numel = _torch_dtype(b.dtype), b.numel
     for n, rank in enumerate(tensors):
         if len(rank) != b.n_tensors:
             raise ValueError(f"rank {n} lists {len(rank)} tensors; the bucket plan has {b.n_tensors}")
         for t, x in enumerate(rank):
-            _check_tensor(x, f"tensors[{n}][{t}]", b.dtype, b.numel[t])
+            # the common case costs two comparisons; the message is built only on failure
+            if hasattr(x, "data_ptr") and (x.dtype != want or x.numel() < numel[t]):
+                _check_tensor(x, f"tensors[{n}][{t}]", b.dtype, numel[t])
     flat = [x for rank in tensors for x in rank]
     return _ptr_array(flat)
 

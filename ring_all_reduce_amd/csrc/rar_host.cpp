@@ -1075,6 +1075,80 @@ struct RingPieces {
     }
 };
 
+// Buckets k0 .. k1-1 of per-rank arenas (bucket k of rank n starts at element
+// start[k] of base[n]): the fused pass in one launch, or each ring step in one
+// launch, over every chunk of every bucket in the range (a launch holds up to
+// 65535 rows of one chunk each, so very long ranges take a few).  Every bucket
+// but the plan's last holds B elements, so two chunk tables describe them all.
+rar_status arena_run(rar_buckets_t b, int N, const std::vector<rar_plan_t> &plan_of, char *const base[], int k0,
+                     int k1, rar_algo algo, hipStream_t st)
+{
+    const int es = elem_bytes(b->dtype);
+    const int per = 65535 / N;
+    std::vector<rar::ArenaParams> launches;
+    std::vector<int64_t> max_chunk;
+    for (int a = k0; a < k1; a += per) {
+        const int e = std::min(k1, a + per);
+        rar::ArenaParams p{};
+        p.N = N;
+        p.B = b->per_bucket;
+        p.nb = e - a;
+        for (int n = 0; n < N; ++n)
+            p.base[n] = base[n] + b->start[a] * es;
+        const rar_plan_s *first = plan_of[a], *lastp = plan_of[e - 1];
+        p.full = first->ct;
+        p.last = lastp->ct;
+        p.last_partial = b->elems[e - 1] != b->per_bucket ? 1 : 0;
+        launches.push_back(p);
+        max_chunk.push_back(std::max(first->max_chunk, lastp->max_chunk));
+    }
+    auto launch = [&](rar::ArenaOp op, int s) -> rar_status {
+        for (size_t i = 0; i < launches.size(); ++i) {
+            launches[i].s = s;
+            if (rar::launch_arena(b->dtype, op, launches[i], max_chunk[i], st) != hipSuccess)
+                return RAR_EHIP;
+        }
+        return RAR_OK;
+    };
+    if (algo == RAR_ALGO_FUSED)
+        return launch(rar::kArenaFused, 0);
+    rar_status rc = RAR_OK;
+    for (int s = 0; s < N - 1 && rc == RAR_OK; ++s)
+        rc = launch(s == N - 2 ? rar::kArenaScatterReduceLast : rar::kArenaScatterReduce, s);
+    for (int s = 0; s < N - 1 && rc == RAR_OK; ++s)
+        rc = launch(rar::kArenaAllgather, s);
+    return rc;
+}
+
+// Tensor lists that are per-rank arenas: every rank's tensors lie end to end
+// in the plan's order (views of one flat buffer per rank, the usual layout of
+// gradient buckets) from a 16-byte aligned start, and bucket starts are 16-byte
+// aligned.  base[n] receives rank n's start.
+bool tensors_form_arenas(rar_buckets_t b, int N, void *const tensors[], char *base[])
+{
+    const int es = elem_bytes(b->dtype);
+    if ((b->per_bucket * es) % 16 != 0)
+        return false;
+    for (int n = 0; n < N; ++n) {
+        char *b0 = nullptr;
+        int64_t cum = 0;
+        for (int t = 0; t < b->n_tensors; ++t) {
+            if (b->numel[t] > 0) {
+                char *p = static_cast<char *>(tensors[(int64_t)n * b->n_tensors + t]);
+                if (!b0)
+                    b0 = p;  // every earlier tensor is empty: this one starts the arena
+                if (p != b0 + cum * es)
+                    return false;
+            }
+            cum += b->numel[t];
+        }
+        if (!b0 || ((uintptr_t)b0 & 15))
+            return false;
+        base[n] = b0;
+    }
+    return true;
+}
+
 // Buckets whose ring steps run on their pieces in place: binary32 at N >= 2
 // (bf16 keeps its partial sums in a plan's workspace and goes through bucket
 // buffers; one rank has no transfers).
@@ -1105,6 +1179,9 @@ extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chun
             rc = check_tensors_disjoint(b, N, tensors);
             if (rc != RAR_OK)
                 return rc;
+            char *base[kMaxRanks];
+            if (tensors_form_arenas(b, N, tensors, base))
+                return arena_run(b, N, plan_of, base, 0, nb, ring_direct ? RAR_ALGO_RING : RAR_ALGO_FUSED, st);
             if (ring_direct) {
                 RingPieces rp(N, st);
                 for (int k = 0; k < nb && rc == RAR_OK; ++k)
@@ -1159,52 +1236,24 @@ extern "C" rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chu
         if (rc != RAR_OK)
             return rc;
         hipStream_t st = static_cast<hipStream_t>(stream);
-        if (algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N)) {
-            // every chunk of every bucket is one job; the buckets between two
-            // ready events share launches
-            JobBatch jb(b->dtype, N, st);
-            char *first[kMaxRanks];
+        if ((algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N)) || ring_on_pieces(b->dtype, N, algo)) {
+            // the buckets between two ready events share the launches
+            char *base[kMaxRanks];
+            for (int n = 0; n < N; ++n)
+                base[n] = static_cast<char *>(arenas[n]);
+            int k0 = 0;
             for (int k = 0; k < nb; ++k) {
                 if (ready_events && ready_events[k]) {
-                    rc = jb.flush();
+                    rc = arena_run(b, N, plan_of, base, k0, k, algo, st);
                     if (rc != RAR_OK)
                         return rc;
                     const hipError_t e = hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0);
                     if (e != hipSuccess)
                         return hip_failed(e);
-                }
-                const rar_plan_s *pl = plan_of[k];
-                for (int c = 0; c < N; ++c) {
-                    for (int n = 0; n < N; ++n)
-                        first[n] = static_cast<char *>(arenas[n]) + (b->start[k] + pl->ct.off[c]) * es;
-                    rc = jb.add(pl->ct.off[c + 1] - pl->ct.off[c], c, first);
-                    if (rc != RAR_OK)
-                        return rc;
+                    k0 = k;
                 }
             }
-            return jb.flush();
-        }
-        if (ring_on_pieces(b->dtype, N, algo)) {
-            // the buckets between two ready events run their ring steps together
-            RingPieces rp(N, st);
-            char *first[kMaxRanks];
-            for (int k = 0; k < nb; ++k) {
-                if (ready_events && ready_events[k]) {
-                    rc = rp.flush();
-                    if (rc != RAR_OK)
-                        return rc;
-                    const hipError_t e = hipStreamWaitEvent(st, static_cast<hipEvent_t>(ready_events[k]), 0);
-                    if (e != hipSuccess)
-                        return hip_failed(e);
-                }
-                const rar_plan_s *pl = plan_of[k];
-                for (int c = 0; c < N; ++c) {
-                    for (int n = 0; n < N; ++n)
-                        first[n] = static_cast<char *>(arenas[n]) + (b->start[k] + pl->ct.off[c]) * es;
-                    rp.add(pl->ct.off[c + 1] - pl->ct.off[c], c, first);
-                }
-            }
-            return rp.flush();
+            return arena_run(b, N, plan_of, base, k0, nb, algo, st);
         }
         void *slice[kMaxRanks];
         for (int k = 0; k < nb; ++k) {

@@ -92,6 +92,24 @@ struct StepJobsParams {
     int N;
 };
 
+// Consecutive buckets of per-rank arenas: rank n's bucket k starts at element
+// k*B of base[n], and the piece of bucket k, chunk c is elements
+// [k*B + off[c], k*B + off[c+1]) in every rank, off from `full`, or from `last`
+// for the final bucket when last_partial.  Workgroup row y is bucket y / N,
+// chunk y % N.
+struct ArenaParams {
+    void *base[kMaxRanks];
+    ChunkTable full;
+    ChunkTable last;
+    int64_t B;
+    int nb;
+    int last_partial;
+    int N;
+    int s;  // ring step within its phase
+};
+
+enum ArenaOp { kArenaFused = 0, kArenaScatterReduce = 1, kArenaScatterReduceLast = 2, kArenaAllgather = 3 };
+
 // Single reducer (prior art): rank 0 accumulates rank `src`.
 struct PairParams {
     RankPtrs bufs;
@@ -110,6 +128,9 @@ hipError_t launch_sr_step(rar_dtype dt, const StepParams &p, bool first, bool la
 hipError_t launch_copy(const CopyParams &p, int max_blocks, int64_t max_job_bytes, hipStream_t st);
 hipError_t launch_pair_add(const PairParams &p, bool last, bool sgd, int max_blocks, hipStream_t st);
 hipError_t launch_sr_jobs(const StepJobsParams &p, bool last, int64_t max_len, hipStream_t st);
+// op kArenaFused: dt either, N with a grouped kernel (bucket_jobs_supported);
+// the ring ops: binary32, any N >= 2.
+hipError_t launch_arena(rar_dtype dt, ArenaOp op, const ArenaParams &p, int64_t max_chunk, hipStream_t st);
 // The binary32 workspace held in the library's static device array: its
 // address on `device`, which must be the current device (looked up on the
 // first call for that device, then kept).

@@ -869,23 +869,22 @@ __global__ __launch_bounds__(kThreads) void rar_sr_step_bf16(StepParams p)
 // carries any number of them.
 // ---------------------------------------------------------------------------
 
-template <bool LAST>
-__global__ __launch_bounds__(kThreads) void rar_sr_jobs_f32(StepJobsParams p)
+// One transfer of a ring step over n binary32 elements: ADD (scatter-reduce:
+// the receiver's dp += the sender's sp, then / N when LAST) or a plain copy
+// (all-gather: the receiver's dp = sp), tiles bx, bx+gx, ... of the body.
+template <bool ADD, bool LAST>
+__device__ __forceinline__ void step_span_f32(const float *sp, float *dp, int64_t n, float fN, int64_t bx,
+                                              int64_t gx)
 {
-    const StepJob jb = p.job[blockIdx.y];
-    const float *sp = jb.src;
-    float *dp = jb.dst;
-    const int64_t n = jb.len;
-    const float fN = (float)p.N;
     auto elem = [&](int64_t e) {
-        float v = dp[e] + sp[e];
+        float v = ADD ? dp[e] + sp[e] : sp[e];
         if (LAST)
             v = v / fN;
         dp[e] = v;
     };
     if ((((uintptr_t)sp ^ (uintptr_t)dp) & 15) != 0) {
         // the two ranks' pieces differ in their 16-byte alignment
-        for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += (int64_t)gridDim.x * kThreads)
+        for (int64_t e = bx * kThreads + threadIdx.x; e < n; e += gx * kThreads)
             elem(e);
         return;
     }
@@ -896,7 +895,7 @@ __global__ __launch_bounds__(kThreads) void rar_sr_jobs_f32(StepJobsParams p)
         h = n;
     const int64_t nvec = (n - h) / 4;
     const int64_t tail0 = h + nvec * 4;
-    if (blockIdx.x == 0) {
+    if (bx == 0) {
         const int t = threadIdx.x;
         if (t < 32) {
             if (t < h)
@@ -908,15 +907,76 @@ __global__ __launch_bounds__(kThreads) void rar_sr_jobs_f32(StepJobsParams p)
     const f32x4 *s4 = reinterpret_cast<const f32x4 *>(sp + h);
     f32x4 *d4 = reinterpret_cast<f32x4 *>(dp + h);
     const int64_t ntiles = (nvec + kThreads - 1) / kThreads;
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    for (int64_t t = bx; t < ntiles; t += gx) {
         const int64_t v = t * kThreads + threadIdx.x;
         if (v < nvec) {
-            f32x4 x = ld(d4 + v) + ld(s4 + v);
+            f32x4 x = ADD ? ld(d4 + v) + ld(s4 + v) : ld(s4 + v);
             if (LAST)
                 x = x / fN;
             st(d4 + v, x);
         }
     }
+}
+
+template <bool LAST>
+__global__ __launch_bounds__(kThreads) void rar_sr_jobs_f32(StepJobsParams p)
+{
+    const StepJob jb = p.job[blockIdx.y];
+    step_span_f32<true, LAST>(jb.src, jb.dst, jb.len, (float)p.N, blockIdx.x, gridDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// Consecutive buckets of per-rank arenas, one launch for all of them: row y
+// of the grid is bucket y / N, chunk y % N, so no job table is needed.  The
+// fused pass runs the grouped body of the flat kernels on each piece (fold
+// from rank c, same bits); a ring step moves each piece from its sender to
+// its receiver ([Gibiansky] §Scatter-reduce and §Allgather, per chunk of
+// each bucket).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void arena_piece(const ArenaParams &p, int k, int c, int64_t &e0, int64_t &len)
+{
+    const bool last = p.last_partial && k == p.nb - 1;
+    const int64_t lo = last ? p.last.off[c] : p.full.off[c];
+    const int64_t hi = last ? p.last.off[c + 1] : p.full.off[c + 1];
+    e0 = (int64_t)k * p.B + lo;
+    len = hi - lo;
+}
+
+template <typename T, int NT, int G>
+__global__ __launch_bounds__(kThreads *G) void rar_arena_fused(ArenaParams p)
+{
+    constexpr int SLOT = sizeof(T) == 4 ? 1 : 2;
+    __shared__ f32x4 chain[G > 1 ? SLOT * kThreads : 1];
+    __shared__ f32x4 mean[G > 1 ? SLOT * kThreads : 1];
+    const int k = blockIdx.y / NT, c = blockIdx.y % NT;
+    int64_t e0, len;
+    arena_piece(p, k, c, e0, len);
+    if (len <= 0)
+        return;
+    auto base = [&](int r) { return static_cast<T *>(p.base[r]) + e0; };
+    if constexpr (sizeof(T) == 4)
+        grouped_span_f32<NT, G, false>(base, nullptr, 0.f, c, len, blockIdx.x, gridDim.x, chain, mean);
+    else
+        grouped_span_bf16<NT, G, false>(base, nullptr, 0.f, c, len, blockIdx.x, gridDim.x, chain, mean);
+}
+
+template <int OP>
+__global__ __launch_bounds__(kThreads) void rar_arena_ring_f32(ArenaParams p)
+{
+    const int N = p.N;
+    const int k = blockIdx.y / N, c = blockIdx.y - k * N;
+    int64_t e0, len;
+    arena_piece(p, k, c, e0, len);
+    if (len <= 0)
+        return;
+    // scatter-reduce step s: rank (c+s) sends chunk c to rank (c+s+1);
+    // all-gather step s: rank (c+s-1) sends it to rank (c+s)
+    const int src = OP == kArenaAllgather ? (c + p.s - 1 + N) % N : (c + p.s) % N;
+    const int dst = OP == kArenaAllgather ? (c + p.s) % N : (c + p.s + 1) % N;
+    step_span_f32<OP != kArenaAllgather, OP == kArenaScatterReduceLast>(
+        static_cast<const float *>(p.base[src]) + e0, static_cast<float *>(p.base[dst]) + e0, len, (float)N,
+        blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1237,6 +1297,51 @@ hipError_t launch_sr_jobs(const StepJobsParams &p, bool last, int64_t max_len, h
         hipLaunchKernelGGL((rar_sr_jobs_f32<true>), g, dim3(kThreads), 0, st, p);
     else
         hipLaunchKernelGGL((rar_sr_jobs_f32<false>), g, dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int NT>
+hipError_t arena_fused_n(rar_dtype dt, const ArenaParams &p, int64_t max_chunk, hipStream_t st)
+{
+    const int rows = p.nb * NT;
+    if (dt == RAR_F32) {
+        constexpr int G = groups_f32(NT);
+        const dim3 g(blocks_x(1 << 24, rows, max_chunk / 4 + 1, 1), rows), b(kThreads * G);
+        hipLaunchKernelGGL((rar_arena_fused<float, NT, G>), g, b, 0, st, p);
+    } else {
+        constexpr int G = groups_bf16(NT);
+        const dim3 g(blocks_x(1 << 24, rows, max_chunk / 8 + 1, 1), rows), b(kThreads * G);
+        hipLaunchKernelGGL((rar_arena_fused<uint16_t, NT, G>), g, b, 0, st, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_arena(rar_dtype dt, ArenaOp op, const ArenaParams &p, int64_t max_chunk, hipStream_t st)
+{
+    if (p.nb <= 0)
+        return hipSuccess;
+    if (op == kArenaFused) {
+        switch (p.N) {
+        case 2: return arena_fused_n<2>(dt, p, max_chunk, st);
+        case 4: return arena_fused_n<4>(dt, p, max_chunk, st);
+        case 8: return arena_fused_n<8>(dt, p, max_chunk, st);
+        case 10: return arena_fused_n<10>(dt, p, max_chunk, st);
+        case 16: return arena_fused_n<16>(dt, p, max_chunk, st);
+        case 40: return arena_fused_n<40>(dt, p, max_chunk, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (dt != RAR_F32 || p.N < 2)
+        return hipErrorInvalidValue;
+    const int rows = p.nb * p.N;
+    const dim3 g(blocks_x(1 << 24, rows, max_chunk / 4 + 1, 1), rows);
+    switch (op) {
+    case kArenaScatterReduce: hipLaunchKernelGGL((rar_arena_ring_f32<kArenaScatterReduce>), g, dim3(kThreads), 0, st, p); break;
+    case kArenaScatterReduceLast:
+        hipLaunchKernelGGL((rar_arena_ring_f32<kArenaScatterReduceLast>), g, dim3(kThreads), 0, st, p);
+        break;
+    default: hipLaunchKernelGGL((rar_arena_ring_f32<kArenaAllgather>), g, dim3(kThreads), 0, st, p); break;
+    }
     return hipGetLastError();
 }
 

@@ -935,16 +935,17 @@ def test_buckets_with_tiny_and_empty_tensors(dt, mode):
 # synchronisation, no memset), so it can be captured and replayed
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("path", ["fused_sgd", "ring_sgd", "bf16_ring_sgd", "bucket_tensors"])
+@pytest.mark.parametrize("path", ["fused_sgd", "ring_sgd", "bf16_ring_sgd", "bucket_tensors", "bucket_tensors_ring"])
 def test_graph_capture_replays_match_eager(path):
     N = 8
-    if path == "bucket_tensors":
+    if path.startswith("bucket_tensors"):
         specs = synth.transformer_tensors(1, d=64, h=256, V=900)
         numels = [s.numel for s in specs]
         b = api.rar_bucket_plan(numels, api.F32, 4 * 20_000)
         pristine = [[torch.randn(k, device=DEV) for k in numels] for _ in range(N)]
         live = [[t.clone() for t in rank] for rank in pristine]
-        run = lambda: api.rar_bucket_allreduce_mean(b, live, None)
+        algo = api.RING if path.endswith("ring") else api.FUSED
+        run = lambda: api.rar_bucket_allreduce_mean(b, live, None, api.BALANCED, algo)
         restore = lambda: [t.copy_(p) for rl, rp in zip(live, pristine) for t, p in zip(rl, rp)]
         state = lambda: torch.cat([t.reshape(-1) for rank in live for t in rank]).clone()
     else:
@@ -984,6 +985,72 @@ def test_graph_capture_replays_match_eager(path):
         torch.cuda.synchronize()
         got = state()
         assert torch.equal(got.view(torch.int32), eager.view(torch.int32)), f"{path}: replay {rep} differs"
+
+
+def _random_bucket_cases(count=32, seed=77):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        N = int(rng.choice([2, 3, 4, 5, 8, 10, 16, 40]))
+        dt = api.F32 if i % 3 else api.BF16
+        algo = api.RING if i % 2 else api.FUSED
+        mode = int(rng.integers(0, 3))
+        n_t = int(rng.integers(1, 13))
+        numels = [int(x) for x in rng.integers(0, 20_000, n_t)]
+        numels[int(rng.integers(0, n_t))] += 1  # at least one element in all
+        # from one element per bucket up, but at most ~200 buckets per case
+        bucket_elems = max(int(rng.choice([1, 7, 64, 999, 4096, 30_001])), -(-sum(numels) // 200))
+        views = bool(rng.integers(0, 2))
+        cases.append((N, dt, algo, mode, tuple(numels), bucket_elems, views, int(rng.integers(0, 1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("N,dt,algo,mode,numels,bucket_elems,views,seed", _random_bucket_cases())
+def test_random_bucket_layouts_bit_exact(N, dt, algo, mode, numels, bucket_elems, views, seed):
+    # random tensor lists (empty tensors included), bucket sizes from one
+    # element up, every chunking, the fused and ring algorithms, tensors as
+    # views of one arena per rank (adjacent pieces merge) or as separate
+    # allocations: every element of every rank bit for bit against the
+    # oracle's ring run bucket by bucket
+    es = 4 if dt == api.F32 else 2
+    tdt = torch.float32 if dt == api.F32 else torch.bfloat16
+    rng = np.random.default_rng(seed)
+    total = sum(numels)
+    if dt == api.F32:
+        host = [rng.standard_normal(total).astype(np.float32) for _ in range(N)]
+    else:
+        host = [oracle.f32_to_bf16(rng.standard_normal(total).astype(np.float32)) for _ in range(N)]
+    cut = np.cumsum([0] + list(numels))
+    keep, tensors = [], []
+    for n in range(N):
+        src = torch.from_numpy(host[n].view(np.int16) if dt == api.BF16 else host[n].copy()).to(DEV)
+        src = src.view(tdt) if dt == api.BF16 else src
+        if views:
+            keep.append(src)
+            tensors.append([src[cut[t]:cut[t + 1]] for t in range(len(numels))])
+        else:
+            tensors.append([src[cut[t]:cut[t + 1]].clone() for t in range(len(numels))])
+    b = api.rar_bucket_plan(list(numels), dt, es * bucket_elems)
+    _, mx = api.rar_bucket_count(b)
+    bufs = [torch.empty(max(mx, 1), dtype=tdt, device=DEV) for _ in range(N)]
+    api.rar_bucket_allreduce_mean(b, tensors, bufs, mode, algo)
+    torch.cuda.synchronize()
+    ref = [h.copy() for h in host]
+    pos = 0
+    for segs in oracle.bucket_layout(list(numels), es, es * bucket_elems):
+        size = sum(sg[3] for sg in segs)
+        part = [np.ascontiguousarray(r[pos:pos + size]) for r in ref]
+        if dt == api.F32:
+            oracle.ring_allreduce_f32(part, oracle.partition(N, size, mode, 4))
+        else:
+            oracle.ring_allreduce_bf16(part, oracle.partition(N, size, mode, 2))
+        for n in range(N):
+            ref[n][pos:pos + size] = part[n]
+        pos += size
+    for n in range(N):
+        got = torch.cat([t.reshape(-1) for t in tensors[n]]) if total else torch.empty(0, dtype=tdt, device=DEV)
+        got = got.cpu().numpy() if dt == api.F32 else _bits16(got)
+        _assert_bits(got, ref[n], f"rank {n}")
 
 
 # ---------------------------------------------------------------------------

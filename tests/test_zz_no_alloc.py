@@ -94,3 +94,39 @@ def test_noalloc_ring_binary32_and_size_limit():
         api.rar_allreduce_ring_noalloc(api.rar_plan(2, big, api.BF16), [0x10000000, 0x10000000 + (1 << 30)], None,
                                        0.1, big)
     assert e.value.status == api.ETOOLARGE
+
+
+def test_noalloc_ring_replays_from_a_hip_graph():
+    # the callers it is for capture their step in a graph: after one eager
+    # call (which looks the workspace up), the captured call replays with
+    # the eager call's bits, with unrelated eager work between replays
+    N, P, lr = 8, 1_000_003, 1e-3
+    plan = api.rar_plan(N, P, api.BF16)
+    pristine = _dev(_bf16_host(N, P, 91))
+    w0 = torch.linspace(-0.02, 0.02, P, device=DEV)
+    live = [t.clone() for t in pristine]
+    w = w0.clone()
+    run = lambda: api.rar_allreduce_ring_noalloc(plan, live, w, lr, P)
+    restore = lambda: ([t.copy_(p) for t, p in zip(live, pristine)], w.copy_(w0))
+    state = lambda: torch.cat([t.view(torch.int16).float() for t in live] + [w]).clone()
+    restore()
+    run()
+    torch.cuda.synchronize()
+    eager = state()
+    restore()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        restore()
+        torch.cuda.synchronize()
+        _ = torch.randn(1000, device=DEV).sum().item()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(state().view(torch.int32), eager.view(torch.int32)), f"replay {rep} differs"
