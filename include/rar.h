@@ -37,9 +37,12 @@
  * enqueueing; they never synchronise, except rar_rank_stride_tune, which
  * times work on its stream and waits for it.  Rank buffers, weights and bucket
  * buffers must be 16-byte aligned; bucket tensors need only element
- * alignment.  The only device allocation is the binary32 workspace of a
- * bf16 plan set to RAR_ALGO_RING (rar_plan_set_algo, or a bucket call that
- * builds such a plan for itself); it lives until the plan is destroyed.
+ * alignment.  The only device allocations are binary32 workspaces of bf16
+ * rings: a bf16 plan set to RAR_ALGO_RING (rar_plan_set_algo, or a bucket call
+ * that builds such a plan for itself), which lives until the plan is
+ * destroyed, and a bf16 RAR_ALGO_RING bucket call over per-rank arenas (one
+ * float per element of the plan, kept with the bucket handle until it is
+ * destroyed).
  *
  * Graph capture: the execute and bucket calls only enqueue kernels and
  * stream waits (no allocation, synchronisation or memset), so they can be
@@ -304,7 +307,12 @@ rar_status rar_bucket_unpack(rar_buckets_t b, int bucket, int N, void *const buc
  * [Gibiansky] §Scatter-reduce and §Allgather run on those same pieces in
  * place (5*(N-1)*size*4 bytes moved per bucket, no packing); each step is
  * a few launches over the pieces of every bucket, so the tensors must again
- * be pairwise disjoint, and bucket_bufs may be NULL.
+ * be pairwise disjoint, and bucket_bufs may be NULL.  When every rank's
+ * tensors lie end to end in the plan's order (views of one flat buffer per
+ * rank, 16-byte aligned, with 16-byte aligned bucket starts), the call runs
+ * as rar_bucket_allreduce_arena over those buffers, also for bf16 with
+ * RAR_ALGO_RING (no packing; binary32 partial sums in a workspace kept with
+ * the bucket handle).
  * Otherwise each bucket is packed into bucket_bufs[n] (N device buffers of at
  * least max_bucket_elems elements, 16-byte aligned, reused by every bucket,
  * overlapping neither each other nor the tensors: RAR_EINVAL), reduced with
@@ -326,8 +334,10 @@ rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chunking chunki
  * (RAR_EALIGN otherwise; a bucket size that is a multiple of 16 bytes gives
  * that), and the N arenas (total elements each) must not overlap
  * (RAR_EINVAL).  With RAR_ALGO_FUSED and N in {2, 4, 8, 10, 16, 40}, and
- * with RAR_ALGO_RING, RAR_F32 and N >= 2 (ring steps over every chunk of those
- * buckets at once), the buckets between two ready events share launches.
+ * with RAR_ALGO_RING and N >= 2 (each ring step over every chunk of those
+ * buckets at once; bf16 keeps the binary32 partial sums in a workspace of one
+ * float per element, allocated on the first such call and kept with the
+ * bucket handle), the buckets between two ready events share launches.
  * Results are bit-identical to rar_allreduce_mean on each slice. */
 rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chunking chunking, rar_algo algo,
                                       void *const arenas[], void *const ready_events[], void *stream);

@@ -588,12 +588,15 @@ struct rar_buckets_s {
     std::vector<int64_t> start, elems;
     std::vector<std::vector<Segment>> segs;
     int64_t max_elems = 0;
-    std::mutex mu;  // guards the plan cache
+    std::mutex mu;  // guards the plan cache and the workspace
     std::map<std::tuple<int, int64_t, int, int>, rar_plan_t> plans;
+    float *ws = nullptr;  // bf16 ring over arenas: binary32 partial sums, `total` floats
     ~rar_buckets_s()
     {
         for (auto &kv : plans)
             rar_plan_destroy(kv.second);
+        if (ws)
+            (void)hipFree(ws);
     }
 };
 
@@ -1085,6 +1088,20 @@ rar_status arena_run(rar_buckets_t b, int N, const std::vector<rar_plan_t> &plan
 {
     const int es = elem_bytes(b->dtype);
     const int per = 65535 / N;
+    float *ws = nullptr;
+    if (algo == RAR_ALGO_RING && b->dtype == RAR_BF16 && k1 > k0) {
+        // the binary32 partial sums of a bf16 ring: allocated on first use,
+        // kept with the buckets
+        std::lock_guard<std::mutex> lock(b->mu);
+        if (!b->ws) {
+            void *p = nullptr;
+            const hipError_t e = hipMalloc(&p, (size_t)b->total * sizeof(float));
+            if (e != hipSuccess)
+                return hip_failed(e);
+            b->ws = static_cast<float *>(p);
+        }
+        ws = b->ws;
+    }
     std::vector<rar::ArenaParams> launches;
     std::vector<int64_t> max_chunk;
     for (int a = k0; a < k1; a += per) {
@@ -1099,6 +1116,7 @@ rar_status arena_run(rar_buckets_t b, int N, const std::vector<rar_plan_t> &plan
         p.full = first->ct;
         p.last = lastp->ct;
         p.last_partial = b->elems[e - 1] != b->per_bucket ? 1 : 0;
+        p.ws = ws ? ws + b->start[a] : nullptr;
         launches.push_back(p);
         max_chunk.push_back(std::max(first->max_chunk, lastp->max_chunk));
     }
@@ -1113,8 +1131,14 @@ rar_status arena_run(rar_buckets_t b, int N, const std::vector<rar_plan_t> &plan
     if (algo == RAR_ALGO_FUSED)
         return launch(rar::kArenaFused, 0);
     rar_status rc = RAR_OK;
-    for (int s = 0; s < N - 1 && rc == RAR_OK; ++s)
-        rc = launch(s == N - 2 ? rar::kArenaScatterReduceLast : rar::kArenaScatterReduce, s);
+    for (int s = 0; s < N - 1 && rc == RAR_OK; ++s) {
+        const bool first = s == 0, last = s == N - 2;
+        rc = launch(first && last ? rar::kArenaScatterReduceFirstLast
+                    : first       ? rar::kArenaScatterReduceFirst
+                    : last        ? rar::kArenaScatterReduceLast
+                                  : rar::kArenaScatterReduce,
+                    s);
+    }
     for (int s = 0; s < N - 1 && rc == RAR_OK; ++s)
         rc = launch(rar::kArenaAllgather, s);
     return rc;
@@ -1163,7 +1187,10 @@ extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chun
         if (!b || !valid_bucket_call(N, chunking, algo))
             return RAR_EINVAL;
         const int nb = (int)b->segs.size();
-        const bool ring_direct = ring_on_pieces(b->dtype, N, algo);
+        // host arithmetic on the given addresses only; validated below
+        char *base[kMaxRanks];
+        const bool arenas = tensors && tensors_form_arenas(b, N, tensors, base);
+        const bool ring_direct = ring_on_pieces(b->dtype, N, algo) || (algo == RAR_ALGO_RING && N >= 2 && arenas);
         const bool direct = (algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N)) || ring_direct;
         for (int k = 0; k < nb; ++k) {
             rar_status rc = check_bucket_args(b, k, N, tensors, bucket_bufs, !direct);
@@ -1179,8 +1206,7 @@ extern "C" rar_status rar_bucket_allreduce_mean(rar_buckets_t b, int N, rar_chun
             rc = check_tensors_disjoint(b, N, tensors);
             if (rc != RAR_OK)
                 return rc;
-            char *base[kMaxRanks];
-            if (tensors_form_arenas(b, N, tensors, base))
+            if (arenas)
                 return arena_run(b, N, plan_of, base, 0, nb, ring_direct ? RAR_ALGO_RING : RAR_ALGO_FUSED, st);
             if (ring_direct) {
                 RingPieces rp(N, st);
@@ -1236,7 +1262,7 @@ extern "C" rar_status rar_bucket_allreduce_arena(rar_buckets_t b, int N, rar_chu
         if (rc != RAR_OK)
             return rc;
         hipStream_t st = static_cast<hipStream_t>(stream);
-        if ((algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N)) || ring_on_pieces(b->dtype, N, algo)) {
+        if ((algo == RAR_ALGO_FUSED && rar::bucket_jobs_supported(N)) || (algo == RAR_ALGO_RING && N >= 2)) {
             // the buckets between two ready events share the launches
             char *base[kMaxRanks];
             for (int n = 0; n < N; ++n)

@@ -105,10 +105,19 @@ struct ArenaParams {
     int nb;
     int last_partial;
     int N;
-    int s;  // ring step within its phase
+    int s;      // ring step within its phase
+    float *ws;  // bf16 ring: binary32 partial sums, indexed like the arenas' elements
 };
 
-enum ArenaOp { kArenaFused = 0, kArenaScatterReduce = 1, kArenaScatterReduceLast = 2, kArenaAllgather = 3 };
+// The first scatter-reduce step differs only for bf16 (partial sums start in ws).
+enum ArenaOp {
+    kArenaFused = 0,
+    kArenaScatterReduce = 1,
+    kArenaScatterReduceLast = 2,
+    kArenaAllgather = 3,
+    kArenaScatterReduceFirst = 4,
+    kArenaScatterReduceFirstLast = 5
+};
 
 // Single reducer (prior art): rank 0 accumulates rank `src`.
 struct PairParams {
@@ -129,7 +138,7 @@ hipError_t launch_copy(const CopyParams &p, int max_blocks, int64_t max_job_byte
 hipError_t launch_pair_add(const PairParams &p, bool last, bool sgd, int max_blocks, hipStream_t st);
 hipError_t launch_sr_jobs(const StepJobsParams &p, bool last, int64_t max_len, hipStream_t st);
 // op kArenaFused: dt either, N with a grouped kernel (bucket_jobs_supported);
-// the ring ops: binary32, any N >= 2.
+// the ring ops: any N >= 2, bf16 with p.ws set.
 hipError_t launch_arena(rar_dtype dt, ArenaOp op, const ArenaParams &p, int64_t max_chunk, hipStream_t st);
 // The binary32 workspace held in the library's static device array: its
 // address on `device`, which must be the current device (looked up on the

@@ -786,19 +786,13 @@ __global__ __launch_bounds__(kThreads) void rar_sr_step_f32(StepParams p)
 // chunk-indexed array serves all ranks).  FIRST: ws = own + sender's bf16;
 // later: ws = own + ws; LAST: the owner's bf16 chunk receives the rounded
 // mean, and the update uses the binary32 mean.
+// Elements [e0, e1) of one transfer: sp, dp, ws (and w) are indexed by the
+// same element index e.
 template <bool FIRST, bool LAST, bool SGD>
-__global__ __launch_bounds__(kThreads) void rar_sr_step_bf16(StepParams p)
+__device__ __forceinline__ void sr_step_bf16_span(const uint16_t *sp, uint16_t *dp, float *ws, float *w, float lr,
+                                                  int N, int64_t e0, int64_t e1)
 {
     constexpr int VPT = 1;
-    const int N = p.N;
-    const int c = blockIdx.y;
-    const int src = (c + p.s) % N;
-    const int dst = (c + p.s + 1) % N;
-    const uint16_t *sp = static_cast<const uint16_t *>(p.bufs.p[src]);
-    uint16_t *dp = static_cast<uint16_t *>(p.bufs.p[dst]);
-    float *ws = p.ws;
-    float *w = p.w;
-
     auto elem = [&](int64_t e) {
         const float incoming = FIRST ? bf16_one(sp[e]) : ws[e];
         const float v = bf16_one(dp[e]) + incoming;
@@ -806,7 +800,7 @@ __global__ __launch_bounds__(kThreads) void rar_sr_step_bf16(StepParams p)
             const float m = v / (float)N;
             dp[e] = (uint16_t)bf16_rne(m);
             if (SGD) {
-                const float step = p.lr * m;
+                const float step = lr * m;
                 w[e] = w[e] - step;
             }
         } else {
@@ -847,7 +841,7 @@ __global__ __launch_bounds__(kThreads) void rar_sr_step_bf16(StepParams p)
                 sum = sum / (float)N;
                 st(d8 + h[k], narrow4(sum));
                 if (SGD) {
-                    const f32x4 step = p.lr * sum;
+                    const f32x4 step = lr * sum;
                     wv[k] = wv[k] - step;
                     st(wp + h[k], wv[k]);
                 }
@@ -857,7 +851,19 @@ __global__ __launch_bounds__(kThreads) void rar_sr_step_bf16(StepParams p)
         }
     };
 
-    run_span<8, VPT>(p.ct.off[c], p.ct.off[c + 1], elem, tile);
+    run_span<8, VPT>(e0, e1, elem, tile);
+}
+
+template <bool FIRST, bool LAST, bool SGD>
+__global__ __launch_bounds__(kThreads) void rar_sr_step_bf16(StepParams p)
+{
+    const int N = p.N;
+    const int c = blockIdx.y;
+    const int src = (c + p.s) % N;
+    const int dst = (c + p.s + 1) % N;
+    sr_step_bf16_span<FIRST, LAST, SGD>(static_cast<const uint16_t *>(p.bufs.p[src]),
+                                        static_cast<uint16_t *>(p.bufs.p[dst]), p.ws, p.w, p.lr, N, p.ct.off[c],
+                                        p.ct.off[c + 1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -984,14 +990,10 @@ __global__ __launch_bounds__(kThreads) void rar_arena_ring_f32(ArenaParams p)
 // overwrites), bucket pack/unpack, and the single reducer's broadcast.
 // ---------------------------------------------------------------------------
 
+// n bytes from s to d in units of `unit` (2 or 4) bytes; tiles bx, bx+gx, ...
 template <int VPT>
-__global__ __launch_bounds__(kThreads) void rar_copy(CopyParams p)
+__device__ __forceinline__ void copy_span(const char *s, char *d, int64_t n, int unit, int64_t bx, int64_t gx)
 {
-    const CopyJob job = p.job[blockIdx.y];
-    const char *s = static_cast<const char *>(job.src);
-    char *d = static_cast<char *>(job.dst);
-    const int64_t n = job.nbytes;
-    const int unit = p.unit;
     auto copy_unit = [&](int64_t byte) {
         if (unit == 4)
             *reinterpret_cast<uint32_t *>(d + byte) = *reinterpret_cast<const uint32_t *>(s + byte);
@@ -1008,7 +1010,7 @@ __global__ __launch_bounds__(kThreads) void rar_copy(CopyParams p)
         const int64_t head = to_line < n ? to_line : n;
         const int64_t body = (n - head) / 16;
         const int64_t tail0 = head + body * 16;
-        if (blockIdx.x == 0) {
+        if (bx == 0) {
             const int64_t t = threadIdx.x;  // lanes 0..63: head units; 64..71: tail units
             if (t < 64) {
                 if (t * unit < head)
@@ -1021,7 +1023,7 @@ __global__ __launch_bounds__(kThreads) void rar_copy(CopyParams p)
         u32x4 *d4 = reinterpret_cast<u32x4 *>(d + head);
         constexpr int64_t TV = (int64_t)kThreads * VPT;
         const int64_t ntiles = (body + TV - 1) / TV;
-        for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        for (int64_t t = bx; t < ntiles; t += gx) {
             const int64_t v0 = t * TV;
             u32x4 x[VPT];
             if (v0 + TV <= body) {
@@ -1042,9 +1044,45 @@ __global__ __launch_bounds__(kThreads) void rar_copy(CopyParams p)
         }
     } else {
         const int64_t units = n / unit;
-        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < units;
-             i += (int64_t)gridDim.x * kThreads)
+        for (int64_t i = bx * kThreads + threadIdx.x; i < units; i += gx * kThreads)
             copy_unit(i * unit);
+    }
+}
+
+template <int VPT>
+__global__ __launch_bounds__(kThreads) void rar_copy(CopyParams p)
+{
+    const CopyJob job = p.job[blockIdx.y];
+    copy_span<VPT>(static_cast<const char *>(job.src), static_cast<char *>(job.dst), job.nbytes, p.unit, blockIdx.x,
+                   gridDim.x);
+}
+
+// A ring step over every chunk of every bucket of bf16 arenas: the
+// scatter-reduce carries each chunk's binary32 partial sum in ws (one holder
+// per chunk at any step, so one array indexed like the arenas serves every
+// rank), the last step writes the owner's rounded mean, and the all-gather
+// copies it on ([Gibiansky] §Scatter-reduce and §Allgather, per chunk of each
+// bucket).
+template <int OP>
+__global__ __launch_bounds__(kThreads) void rar_arena_ring_bf16(ArenaParams p)
+{
+    const int N = p.N;
+    const int k = blockIdx.y / N, c = blockIdx.y - k * N;
+    int64_t e0, len;
+    arena_piece(p, k, c, e0, len);
+    if (len <= 0)
+        return;
+    const int src = OP == kArenaAllgather ? (c + p.s - 1 + N) % N : (c + p.s) % N;
+    const int dst = OP == kArenaAllgather ? (c + p.s) % N : (c + p.s + 1) % N;
+    const uint16_t *sp = static_cast<const uint16_t *>(p.base[src]);
+    uint16_t *dp = static_cast<uint16_t *>(p.base[dst]);
+    if constexpr (OP == kArenaAllgather) {
+        copy_span<1>(reinterpret_cast<const char *>(sp + e0), reinterpret_cast<char *>(dp + e0), len * 2, 2,
+                     blockIdx.x, gridDim.x);
+    } else {
+        constexpr bool FIRST = OP == kArenaScatterReduceFirst || OP == kArenaScatterReduceFirstLast;
+        constexpr bool LAST = OP == kArenaScatterReduceLast || OP == kArenaScatterReduceFirstLast;
+        sr_step_bf16_span<FIRST, LAST, false>(sp, dp, p.ws, nullptr, 0.f, N, e0, e0 + len);
     }
 }
 
@@ -1331,9 +1369,30 @@ hipError_t launch_arena(rar_dtype dt, ArenaOp op, const ArenaParams &p, int64_t 
         default: return hipErrorInvalidValue;
         }
     }
-    if (dt != RAR_F32 || p.N < 2)
+    if (p.N < 2)
         return hipErrorInvalidValue;
     const int rows = p.nb * p.N;
+    if (dt == RAR_BF16) {
+        if (!p.ws)
+            return hipErrorInvalidValue;
+        const dim3 g(blocks_x(1 << 24, rows, max_chunk / 8 + 1, 1), rows), b(kThreads);
+        switch (op) {
+        case kArenaScatterReduceFirst: hipLaunchKernelGGL((rar_arena_ring_bf16<kArenaScatterReduceFirst>), g, b, 0, st, p); break;
+        case kArenaScatterReduceFirstLast:
+            hipLaunchKernelGGL((rar_arena_ring_bf16<kArenaScatterReduceFirstLast>), g, b, 0, st, p);
+            break;
+        case kArenaScatterReduce: hipLaunchKernelGGL((rar_arena_ring_bf16<kArenaScatterReduce>), g, b, 0, st, p); break;
+        case kArenaScatterReduceLast: hipLaunchKernelGGL((rar_arena_ring_bf16<kArenaScatterReduceLast>), g, b, 0, st, p); break;
+        case kArenaAllgather: hipLaunchKernelGGL((rar_arena_ring_bf16<kArenaAllgather>), g, b, 0, st, p); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    // binary32 partial sums live in the arenas themselves: the first step is a middle one
+    if (op == kArenaScatterReduceFirst)
+        op = kArenaScatterReduce;
+    else if (op == kArenaScatterReduceFirstLast)
+        op = kArenaScatterReduceLast;
     const dim3 g(blocks_x(1 << 24, rows, max_chunk / 4 + 1, 1), rows);
     switch (op) {
     case kArenaScatterReduce: hipLaunchKernelGGL((rar_arena_ring_f32<kArenaScatterReduce>), g, dim3(kThreads), 0, st, p); break;

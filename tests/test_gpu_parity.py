@@ -576,8 +576,9 @@ def test_sixty_four_ranks_sampled(dt):
 # Buckets reduced as a simulated backward pass produces them
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("dt", [api.F32, api.BF16])
 @pytest.mark.parametrize("algo", [api.FUSED, api.RING])
-def test_bucket_arena_waits_for_each_ready_event(algo):
+def test_bucket_arena_waits_for_each_ready_event(algo, dt):
     # The producer stream writes bucket k only after a long matrix product, the
     # arenas start as NaN, and the reduction runs on another stream: a reduction
     # that did not wait for bucket k's event would read NaN and fail parity.
@@ -585,11 +586,17 @@ def test_bucket_arena_waits_for_each_ready_event(algo):
     specs = synth.transformer_tensors(2, d=128, h=512, V=4000)
     numels = [s.numel for s in specs]
     total = sum(numels)
-    bucket_bytes = 4 * 100_000
+    es = 4 if dt == api.F32 else 2
+    bucket_bytes = es * 100_000
     host = [np.random.default_rng(900 + n).standard_normal(total).astype(np.float32) * 1e-3 for n in range(N)]
-    pristine = [torch.from_numpy(h.copy()).to(DEV) for h in host]
-    arenas = [torch.full((total,), float("nan"), device=DEV) for _ in range(N)]
-    b = api.rar_bucket_plan(numels, api.F32, bucket_bytes)
+    if dt == api.BF16:
+        host = [oracle.f32_to_bf16(h) for h in host]
+        pristine = _bf16_dev(host)
+        arenas = [torch.full((total,), float("nan"), device=DEV, dtype=torch.bfloat16) for _ in range(N)]
+    else:
+        pristine = [torch.from_numpy(h.copy()).to(DEV) for h in host]
+        arenas = [torch.full((total,), float("nan"), device=DEV) for _ in range(N)]
+    b = api.rar_bucket_plan(numels, dt, bucket_bytes)
     nb, _ = api.rar_bucket_count(b)
     infos = [api.rar_bucket_info(b, k) for k in range(nb)]
     a = torch.randn(2048, 2048, device=DEV)
@@ -608,11 +615,15 @@ def test_bucket_arena_waits_for_each_ready_event(algo):
     comm.synchronize()
     producer.synchronize()
     for n in range(1, N):
-        assert torch.equal(arenas[n], arenas[0])
-    got = arenas[0].cpu().numpy()
+        assert torch.equal(arenas[n].view(torch.int16 if dt == api.BF16 else torch.int32),
+                           arenas[0].view(torch.int16 if dt == api.BF16 else torch.int32))
+    got = arenas[0].cpu().numpy() if dt == api.F32 else _bits16(arenas[0])
     for (so, el, _) in infos:
         part = [np.ascontiguousarray(h[so:so + el]) for h in host]
-        oracle.ring_allreduce_f32(part, oracle.partition(N, el))
+        if dt == api.F32:
+            oracle.ring_allreduce_f32(part, oracle.partition(N, el))
+        else:
+            oracle.ring_allreduce_bf16(part, oracle.partition(N, el, oracle.BALANCED, 2))
         _assert_bits(got[so:so + el], part[0], f"bucket at {so}")
 
 
