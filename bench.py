@@ -373,6 +373,8 @@ def stream_ref_rows(add, name, ranks, w, w_vpl, vecs, groups, stream, dev):
             {"what": "reference kernel: as above, every lane moving all streams"})
     add(f"{name}_ref_move_in_place_1_stream", 2 * rank_bytes, ref.fn(0, ranks[:1], None, 0, vecs, 1, stream), None,
         {"what": "reference kernel: one stream read and written back in place"})
+    add(f"{name}_ref_copy_1_to_1", 2 * rank_bytes, ref.fn(3, ranks[:2], None, 0, vecs, 1, stream), None,
+        {"what": "reference kernel: rank 0 copied into rank 1, one vector per lane, no job table"})
     add(f"{name}_ref_read_only_{n}_streams_g{groups}", both // 2, ref.fn(2, ranks, w, w_vpl, vecs, groups, stream),
         None, what)
     add(f"{name}_ref_write_only_{n}_streams_g{groups}", both // 2, ref.fn(1, ranks, w, w_vpl, vecs, groups, stream),

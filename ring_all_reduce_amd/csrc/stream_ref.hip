@@ -11,7 +11,9 @@
 //           (the fused pass's bytes and streams exactly);
 //   mode 1  write only (no reads);
 //   mode 2  read only (the loaded data decide whether anything is stored, to a
-//           4 KiB sink, so the loads are not removed).
+//           4 KiB sink, so the loads are not removed);
+//   mode 3  a plain copy of rank 0 into rank 1 (one vector per lane, one tile
+//           per workgroup, no job table): the 1 -> 1 streaming reference.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -105,6 +107,13 @@ __global__ __launch_bounds__(kLanes *G) void sref_streams(SrefParams p)
     }
 }
 
+__global__ __launch_bounds__(kLanes) void sref_copy(SrefParams p)
+{
+    const int64_t v = (int64_t)blockIdx.x * kLanes + threadIdx.x;
+    if (v < p.vecs)
+        st(static_cast<u32x4 *>(p.rank[1]) + v, ld(static_cast<const u32x4 *>(p.rank[0]) + v));
+}
+
 template <int NR, int G, int WV>
 hipError_t launch(int mode, const SrefParams &p, hipStream_t st)
 {
@@ -119,16 +128,17 @@ hipError_t launch(int mode, const SrefParams &p, hipStream_t st)
 
 }  // namespace
 
-// mode: 0 move in place, 1 write only, 2 read only.  ranks: n_ranks device
-// pointers of `vecs` 16-byte vectors each; w: w_vpl * vecs vectors (w_vpl 1
-// for binary32 ranks, 2 for bf16 ranks, 0 for no weight stream); sink: 4 KiB,
-// needed by mode 2.  Shapes: (n_ranks, groups, w_vpl) in {(10,4,1), (10,1,1),
-// (40,4,2), (8,4,0), (1,1,0)}.  Returns 0, -1 for bad arguments, -5 if the
-// launch failed.
+// mode: 0 move in place, 1 write only, 2 read only, 3 copy rank 0 into rank 1.
+// ranks: n_ranks device pointers of `vecs` 16-byte vectors each; w: w_vpl *
+// vecs vectors (w_vpl 1 for binary32 ranks, 2 for bf16 ranks, 0 for no weight
+// stream); sink: 4 KiB, needed by mode 2.  Shapes: (n_ranks, groups, w_vpl) in
+// {(10,4,1), (10,1,1), (40,4,2), (8,4,0), (1,1,0)}, and (2,1,0) for mode 3
+// (the two ranks must not overlap).  Returns 0, -1 for bad arguments, -5 if
+// the launch failed.
 extern "C" int sref_run(int mode, int n_ranks, void *const ranks[], void *w, int w_vpl, int64_t vecs, int groups,
                         void *sink, void *stream)
 {
-    if (mode < 0 || mode > 2 || n_ranks < 1 || n_ranks > kMaxRanks || !ranks || vecs < 0 ||
+    if (mode < 0 || mode > 3 || n_ranks < 1 || n_ranks > kMaxRanks || !ranks || vecs < 0 ||
         (vecs > 0 && (vecs + kLanes - 1) / kLanes > 0x7fffffff))
         return -1;
     if ((w_vpl > 0) != (w != nullptr) || (mode == 2 && !sink))
@@ -148,7 +158,13 @@ extern "C" int sref_run(int mode, int n_ranks, void *const ranks[], void *w, int
         return 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (n_ranks == 10 && groups == 4 && w_vpl == 1)
+    if (mode == 3) {
+        const uintptr_t a = (uintptr_t)ranks[0], b = (uintptr_t)ranks[1], bytes = (uintptr_t)vecs * 16;
+        if (n_ranks != 2 || groups != 1 || w_vpl != 0 || (a < b + bytes && b < a + bytes))
+            return -1;
+        hipLaunchKernelGGL(sref_copy, dim3((unsigned)((vecs + kLanes - 1) / kLanes)), dim3(kLanes), 0, st, p);
+        e = hipGetLastError();
+    } else if (n_ranks == 10 && groups == 4 && w_vpl == 1)
         e = launch<10, 4, 1>(mode, p, st);
     else if (n_ranks == 10 && groups == 1 && w_vpl == 1)
         e = launch<10, 1, 1>(mode, p, st);
