@@ -512,7 +512,8 @@ def secondary_rows(dev, stream, reps=5):
                 {"algo": "rs_sgd_ag", **lay}, ring_leg)
             del wreps
             # the ceiling of the fused pass's access pattern on these buffers
-            stream_ref_rows(add, wl.name, bufs, w, 1, P * 4 // 16, 4, stream, dev)
+            optional_rows(rows, f"{wl.name}_ref", lambda: stream_ref_rows(add, wl.name, bufs, w, 1, P * 4 // 16, 4,
+                                                                          stream, dev))
             w = synth.weights(wl, dev)
             del bufs, pool
             torch.cuda.empty_cache()
@@ -555,7 +556,8 @@ def secondary_rows(dev, stream, reps=5):
         add(f"{wl.name}_{an}", nb, lambda: api.rar_allreduce_sgd(plan, bufs, w, wl.lr, P, stream),
             moved_bf_ring if algo == api.RING else None, {"algo": an, **lay}, bf_leg)
         del plan
-    stream_ref_rows(add, wl.name, bufs, w, 2, P * 2 // 16, 4, stream, dev)
+    optional_rows(rows, f"{wl.name}_ref",
+                  lambda: stream_ref_rows(add, wl.name, bufs, w, 2, P * 2 // 16, 4, stream, dev))
     w = synth.weights(wl, dev)
     del bufs, pool
     torch.cuda.empty_cache()
@@ -625,10 +627,25 @@ def secondary_rows(dev, stream, reps=5):
         None, {"buckets": nbk, "rank_layout": "separate allocations"})
     del sep, sep_ranks, tensors
     torch.cuda.empty_cache()
-    for r in overlap_rows(wl, b, infos, arenas, dev, stream, nb):
-        rows.append(r)
-        log(f"row {r['row']}: {r}")
+    def overlap():
+        for r in overlap_rows(wl, b, infos, arenas, dev, stream, nb):
+            rows.append(r)
+            log(f"row {r['row']}: {r}")
+    optional_rows(rows, f"{wl.name}_overlap", overlap)
     return rows
+
+
+def optional_rows(rows, name, fn):
+    """Reference and overlap rows: a failure there (a reference library not
+    built, a CU mask the runtime refuses) is recorded as a row, and the
+    benchmark goes on."""
+    import torch
+    try:
+        fn()
+    except (RuntimeError, OSError) as e:
+        torch.cuda.synchronize()
+        rows.append({"row": name, "error": f"{type(e).__name__}: {e}"})
+        log(f"row {name}: skipped ({e})")
 
 
 def _cu_masked_stream(cus):
@@ -716,6 +733,7 @@ def overlap_rows(wl, b, infos, arenas, dev, stream, nb, reps=3, reserved=(32, 64
 
     rows = [row(f"{wl.name}_overlap_simulated_backward", torch.cuda.Stream(), torch.cuda.Stream(),
                 {"streams": "ordinary (every CU for each)"})]
+    yield rows[0]
     full_prod, full_comm = rows[0]["producer_ms"], rows[0]["allreduce_ms"]
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
@@ -734,7 +752,7 @@ def overlap_rows(wl, b, infos, arenas, dev, stream, nb, reps=3, reserved=(32, 64
             torch.cuda.synchronize()
             hip.hipStreamDestroy(hc)
             hip.hipStreamDestroy(hp)
-    return rows
+        yield r
 
 
 def oracle_timer(kind, bufs, w, lr, sample_elems=20_000_000, bucket_elems=None, one_thread=False):

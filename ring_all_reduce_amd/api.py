@@ -2,7 +2,10 @@
 
 Argument marshalling only -- every step of the all-reduce runs in the HIP
 library.  Device buffers may be given as torch tensors (contiguous, on the
-GPU) or as integer device addresses.  ``stream`` may be a torch stream, an
+GPU, of the plan's element type: float32 for RAR_F32 and for weights,
+bfloat16 for RAR_BF16, with at least as many elements as the call touches;
+ValueError otherwise) or as integer device addresses, which are passed on
+unchecked.  ``stream`` may be a torch stream, an
 integer hipStream_t, or None for torch's current stream on the current
 device (the default stream when torch has no GPU).
 
@@ -347,7 +350,9 @@ def rar_bucket_unpack(b: Buckets, bucket: int, bucket_bufs: Sequence, tensors: S
 def rar_bucket_allreduce_mean(b: Buckets, tensors: Sequence[Sequence], bucket_bufs=None,
                               chunking: int = BALANCED, algo: int = FUSED, stream=None) -> None:
     """bucket_bufs: N buffers of max_bucket_elems, or None when the reduction
-    runs straight from the tensors (RAR_ALGO_FUSED at a supported rank count)."""
+    runs straight from the tensors: RAR_ALGO_FUSED at a supported rank count,
+    RAR_ALGO_RING on binary32 at N >= 2, and RAR_ALGO_RING on bf16 when every
+    rank's tensors lie end to end in one buffer (see rar.h)."""
     if bucket_bufs is not None and b.handle:
         _check_bucket_bufs(b, bucket_bufs, rar_bucket_count(b)[1])
     bufs = None if bucket_bufs is None else _ranks(bucket_bufs, len(tensors), "bucket_bufs")
