@@ -14,8 +14,9 @@
 // that nothing is re-read.
 //
 // Work decomposition, shared by every kernel: blockIdx.y selects a job (a
-// chunk of the chunk table, or a copy segment); blockIdx.x and a grid-stride
-// loop walk that job's element range.  The body of the range starts on a
+// chunk of the chunk table, a bucket piece, a copy segment, or -- for buckets
+// in per-rank arenas -- bucket y / N and its chunk y % N); blockIdx.x and a
+// grid-stride loop walk that job's element range.  The body of the range starts on a
 // 128-byte cache line and is processed in tiles of kThreads*VPT 16-byte
 // vectors, lane-contiguous so that one wave instruction touches 1 KiB of
 // consecutive memory and each tile covers whole lines (no line is fetched or
