@@ -292,6 +292,15 @@ def main():
         if mover:
             out["roofline"]["vs_same_pattern_mover"] = {"row": mover["row"], "mover_GBps": mover["alg_GBps"],
                                                         "frac": round(achieved / mover["alg_GBps"], 4)}
+        # and against the same streams read alone plus written alone, back to
+        # back: the time HBM takes for these bytes if reads and writes never mix
+        rd = next((r for r in out["rows"] if r["row"] == f"{wl.name}_ref_read_only_{N + 1}_streams_g4"), None)
+        wr = next((r for r in out["rows"] if r["row"] == f"{wl.name}_ref_write_only_{N + 1}_streams_g4"), None)
+        if rd and wr:
+            serial = rd["ms"] + wr["ms"]
+            out["roofline"]["vs_read_only_plus_write_only"] = {
+                "rows": [rd["row"], wr["row"]], "serial_ms": round(serial, 4),
+                "serial_GBps": round(nbytes / (serial * 1e-3) / 1e9, 1), "frac": round(serial / kern_ms, 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, dev)
     print(json.dumps(out), flush=True)
