@@ -398,6 +398,19 @@ __global__ __launch_bounds__(kThreads) void rar_fused_bf16(FusedParams p)
 // back-to-back stores, and HBM drains several concurrent write streams
 // faster that way (measured on MI355X, 10 ranks x 300M with SGD: ~5.45 TB/s
 // with one group, ~5.75 TB/s with two to four).
+//
+// How many memory operations a wave keeps in flight matters as well, and here
+// it follows from how the group index is computed.  g = threadIdx.x / kThreads
+// is not known to the compiler to be equal across a wave, so every lane loads
+// its run's rank pointers from the kernel arguments itself, and the wait for
+// each such pointer also waits for all of the wave's earlier loads and stores
+// (one counter covers both): a wave's vector memory operations go out nearly
+// one at a time.  On MI355X that is the fastest form measured.  A wave-uniform
+// index (pointers in scalar registers, everything issued back to back) was
+// 2.6% slower on 10 binary32 ranks and 3.7% slower on 40 bf16 ranks; explicit
+// waits after each load or after each store, with the uniform index, came
+// within 0.6% of this form on those two shapes, but lost up to 3.5% on bf16
+// with two groups (8 and 16 ranks).  So g stays as it is.
 
 // Scalar path for one element e of a span: the whole fold in one lane.
 // base(r) is rank r's element pointer at the span's element 0.
