@@ -13,7 +13,13 @@
 //   mode 2  read only (the loaded data decide whether anything is stored, to a
 //           4 KiB sink, so the loads are not removed);
 //   mode 3  a plain copy of rank 0 into rank 1 (one vector per lane, one tile
-//           per workgroup, no job table): the 1 -> 1 streaming reference.
+//           per workgroup, no job table): the 1 -> 1 streaming reference;
+//   mode 4  move in place as mode 0, for 10 binary32 ranks and the weights
+//           only, with the eleven pointers in one table and each lane
+//           checking its index per access.  The same bytes, streams, groups
+//           and order as mode 0; only the compiled code differs: here each
+//           wave gets two of its stores out at a time, and that form moved
+//           these streams fastest of the movers measured.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -107,6 +113,36 @@ __global__ __launch_bounds__(kLanes *G) void sref_streams(SrefParams p)
     }
 }
 
+// Mode 4: NS streams in one pointer table (the ranks, then w), stream s in
+// group s / PER, one vector per lane and stream.
+struct TableParams {
+    void *s[16];
+    int64_t vecs;
+    uint32_t key;  // 0 at run time, as in SrefParams
+};
+
+template <int NS, int G>
+__global__ __launch_bounds__(kLanes *G) void sref_table_move(TableParams p)
+{
+    constexpr int PER = (NS + G - 1) / G;
+    const int g = threadIdx.x / kLanes, lane = threadIdx.x % kLanes;
+    const int64_t i = (int64_t)blockIdx.x * kLanes + lane;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (g * PER + j < NS)
+            cnt = j + 1;
+    u32x4 x[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (j < cnt && i < p.vecs)
+            x[j] = ld(static_cast<const u32x4 *>(p.s[g * PER + j]) + i);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (j < cnt && i < p.vecs)
+            st(static_cast<u32x4 *>(p.s[g * PER + j]) + i, x[j] ^ p.key);
+}
+
 __global__ __launch_bounds__(kLanes) void sref_copy(SrefParams p)
 {
     const int64_t v = (int64_t)blockIdx.x * kLanes + threadIdx.x;
@@ -128,17 +164,18 @@ hipError_t launch(int mode, const SrefParams &p, hipStream_t st)
 
 }  // namespace
 
-// mode: 0 move in place, 1 write only, 2 read only, 3 copy rank 0 into rank 1.
+// mode: 0 move in place, 1 write only, 2 read only, 3 copy rank 0 into rank 1,
+// 4 move in place from one pointer table.
 // ranks: n_ranks device pointers of `vecs` 16-byte vectors each; w: w_vpl *
 // vecs vectors (w_vpl 1 for binary32 ranks, 2 for bf16 ranks, 0 for no weight
 // stream); sink: 4 KiB, needed by mode 2.  Shapes: (n_ranks, groups, w_vpl) in
-// {(10,4,1), (10,1,1), (40,4,2), (8,4,0), (1,1,0)}, and (2,1,0) for mode 3
-// (the two ranks must not overlap).  Returns 0, -1 for bad arguments, -5 if
-// the launch failed.
+// {(10,4,1), (10,1,1), (40,4,2), (8,4,0), (1,1,0)}, (2,1,0) for mode 3 (the
+// two ranks must not overlap), and (10,4,1) only for mode 4.  Returns 0, -1
+// for bad arguments, -5 if the launch failed.
 extern "C" int sref_run(int mode, int n_ranks, void *const ranks[], void *w, int w_vpl, int64_t vecs, int groups,
                         void *sink, void *stream)
 {
-    if (mode < 0 || mode > 3 || n_ranks < 1 || n_ranks > kMaxRanks || !ranks || vecs < 0 ||
+    if (mode < 0 || mode > 4 || n_ranks < 1 || n_ranks > kMaxRanks || !ranks || vecs < 0 ||
         (vecs > 0 && (vecs + kLanes - 1) / kLanes > 0x7fffffff))
         return -1;
     if ((w_vpl > 0) != (w != nullptr) || (mode == 2 && !sink))
@@ -163,6 +200,17 @@ extern "C" int sref_run(int mode, int n_ranks, void *const ranks[], void *w, int
         if (n_ranks != 2 || groups != 1 || w_vpl != 0 || (a < b + bytes && b < a + bytes))
             return -1;
         hipLaunchKernelGGL(sref_copy, dim3((unsigned)((vecs + kLanes - 1) / kLanes)), dim3(kLanes), 0, st, p);
+        e = hipGetLastError();
+    } else if (mode == 4) {
+        if (n_ranks != 10 || groups != 4 || w_vpl != 1)
+            return -1;
+        TableParams t{};
+        for (int n = 0; n < 10; ++n)
+            t.s[n] = ranks[n];
+        t.s[10] = w;
+        t.vecs = vecs;
+        hipLaunchKernelGGL((sref_table_move<11, 4>), dim3((unsigned)((vecs + kLanes - 1) / kLanes)),
+                           dim3(kLanes * 4), 0, st, t);
         e = hipGetLastError();
     } else if (n_ranks == 10 && groups == 4 && w_vpl == 1)
         e = launch<10, 4, 1>(mode, p, st);
