@@ -54,16 +54,20 @@
  * inside the same capture (on a stream forked from the capturing one).
  *
  * Errors: every argument is checked before any device work is enqueued; on
- * error nothing is enqueued and a negative rar_status is returned.
- * RAR_EHIP means a HIP launch or runtime call failed, RAR_ENOMEM that a
- * device allocation did.  The library clears HIP's last-error state when it
- * returns either, so the caller's next HIP call does not report it again.
+ * an argument error nothing is enqueued and a negative rar_status is
+ * returned.  RAR_EHIP means a HIP launch or runtime call failed, RAR_ENOMEM
+ * that a device allocation did; a call of several launches that fails that
+ * way part-way may leave its earlier launches enqueued, and the buffers'
+ * contents are then unspecified.  The library clears HIP's last-error state
+ * when it returns either, so the caller's next HIP call does not report it
+ * again.
  * Thread safety: a plan is immutable after rar_plan_set_algo; a plan without
  * a workspace may be used from several host threads and streams at once.  A
  * bf16 ring plan owns one workspace and must be used by one stream at a time.
  * A bucket handle may be used from several threads and streams at once (its
  * plan cache is locked), except with dtype bf16 and RAR_ALGO_RING, whose
- * cached plans share one workspace per bucket size: one stream at a time.
+ * binary32 workspaces (one per bucket size for bucket buffers, one per handle
+ * for arenas) are shared by every call: one stream at a time.
  */
 #ifndef RAR_H
 #define RAR_H
