@@ -378,7 +378,7 @@ class StreamRef:
 
 def stream_ref_rows(add, name, ranks, w, w_vpl, vecs, groups, stream, dev):
     """Reference rows over the workload's own buffers (in this order: the
-    write-only row overwrites them)."""
+    write-only rows overwrite them)."""
     ref = StreamRef(dev)
     n = len(ranks) + (1 if w is not None else 0)
     rank_bytes = vecs * 16
@@ -400,8 +400,12 @@ def stream_ref_rows(add, name, ranks, w, w_vpl, vecs, groups, stream, dev):
         {"what": "reference kernel: rank 0 copied into rank 1, one vector per lane, no job table"})
     add(f"{name}_ref_read_only_{n}_streams_g{groups}", both // 2, ref.fn(2, ranks, w, w_vpl, vecs, groups, stream),
         None, what)
+    add(f"{name}_ref_read_only_1_stream", rank_bytes, ref.fn(2, ranks[:1], None, 0, vecs, 1, stream), None,
+        {"what": "reference kernel: one stream read only"})
     add(f"{name}_ref_write_only_{n}_streams_g{groups}", both // 2, ref.fn(1, ranks, w, w_vpl, vecs, groups, stream),
         None, what)
+    add(f"{name}_ref_write_only_1_stream", rank_bytes, ref.fn(1, ranks[:1], None, 0, vecs, 1, stream), None,
+        {"what": "reference kernel: one stream written only"})
 
 
 class CopyCalibration:

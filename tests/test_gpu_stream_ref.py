@@ -55,7 +55,8 @@ def test_reference_kernels_reject_bad_shapes_without_launching():
 
 SHAPES = [  # (mode, ranks, groups, w vectors per lane)
     (0, 10, 4, 1), (0, 10, 1, 1), (0, 40, 4, 2), (0, 8, 4, 0), (0, 1, 1, 0), (4, 10, 4, 1),
-    (1, 10, 4, 1), (1, 10, 1, 1), (1, 40, 4, 2), (2, 10, 4, 1), (2, 40, 4, 2), (3, 2, 1, 0),
+    (1, 10, 4, 1), (1, 10, 1, 1), (1, 40, 4, 2), (1, 1, 1, 0), (2, 10, 4, 1), (2, 40, 4, 2), (2, 1, 1, 0),
+    (3, 2, 1, 0),
 ]
 
 
