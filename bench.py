@@ -8,7 +8,7 @@ One step = one rar_allreduce_sgd call over the whole workload: every rank's
 gradient is averaged in ring order, the mean is written to every rank, and
 the binary32 weights take one SGD step.  Inputs are seeded synthetic vectors
 already resident in HBM when the timed region starts.  The N ranks sit in one
-allocation at the stride rar_rank_stride_tune measures fastest among 12
+allocation at the stride rar_rank_stride_tune measures fastest among 64
 candidates (taken before the timed region); rows keep the static
 rar_rank_stride layout and separately allocated ranks beside it.
 
@@ -70,7 +70,7 @@ def alg_bytes(N, P, es, sgd):
     return 2 * N * P * es + (8 * P if sgd else 0)
 
 
-TUNE_CANDIDATES = 12
+TUNE_CANDIDATES = 64
 TUNE_STATS = {}  # (P, dtype) -> the tuner's per-candidate measurements
 
 
@@ -103,13 +103,15 @@ def layout_note(stride, P, dt, full=False):
     by = {c: (m, sp) for c, m, sp in cands}
     note = {"layout": f"one allocation, rank n at n * {stride} bytes",
             "stride_bytes": stride, "rar_rank_stride_bytes": static,
-            "pick": (f"rar_rank_stride_tune over {len(cands)} strides: the smallest median, unless "
-                     "rar_rank_stride's stride is within the larger of the two spreads")}
+            "pick": (f"rar_rank_stride_tune over {len(cands)} strides: the finalist (the four best of the first "
+                     "8 timings, and rar_rank_stride's stride) with the smallest median of 24 timings, unless "
+                     "rar_rank_stride's stride is within a third of the finalists' median spread")}
     if stride in by:
         note["picked_median_ms"], note["picked_spread_ms"] = round(by[stride][0], 4), round(by[stride][1], 4)
     if static in by:
         note["rar_rank_stride_median_ms"] = round(by[static][0], 4)
         note["rar_rank_stride_spread_ms"] = round(by[static][1], 4)
+
     if full:
         note["candidates_mib_median_spread_ms"] = [[c >> 20, round(m, 4), round(sp, 4)] for c, m, sp in cands]
     return note

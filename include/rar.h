@@ -149,17 +149,24 @@ rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *stride_bytes);
  * s0 + 2 MiB, ... (s0 the smallest multiple of 2 MiB >= P * element size),
  * the first max_candidates (1..RAR_MAX_STRIDE_CANDIDATES) of them for which
  * (N-1) * stride + P * element size <= pool_bytes, and returns the fastest
- * in *stride_bytes (each candidate: one untimed and two timed calls in each
- * of four rounds, forward and backward in turn; the smallest median of the
- * eight wins, ties to the smaller stride -- except that the stride
- * rar_rank_stride gives, when it is a candidate, is kept if its median lies
- * within the winner's by no more than the larger of the two candidates'
- * spreads, the range of the middle six of their eight timings: on MI355X the
- * fast strides lie within about 1% of each other, about as much as single
- * calls vary).  The pool's contents are
- * overwritten; the call enqueues on `stream` and waits for it, so it must
- * not run under graph capture.  N == 1 or P == 0 returns s0
- * without device work.  Which strides are fast differs by shape (see
+ * in *stride_bytes.  Two stages, each in rounds that visit the candidates
+ * forward and backward in turn, one untimed and two timed calls per
+ * candidate and round: four rounds over every candidate, then eight more
+ * over the finalists, the four with the smallest medians so far and the
+ * stride rar_rank_stride gives when it is a candidate (24 timings each).
+ * The finalist with the smallest median wins, ties to the smaller stride --
+ * except that rar_rank_stride's stride is kept if its median exceeds the
+ * winner's by no more than a third of the finalists' typical spread (the
+ * median of their spreads, each the range of the middle three quarters of
+ * its timings), about two standard errors of a difference of two such
+ * medians: on MI355X the fast strides lie within about 1% of each other,
+ * about as much as single calls vary.  Fast strides can lie well past the
+ * first few: at
+ * 10 x 300M fp32 the fastest of 64 were 1192 and 1272 MiB (the 64th), the
+ * SGD call up to 2% faster there than at the static rule's 1146 MiB.  The
+ * pool's contents are overwritten; the call enqueues on `stream` and waits
+ * for it, so it must not run under graph capture.  N == 1 or P == 0 returns
+ * s0 without device work.  Which strides are fast differs by shape (see
  * rar_rank_stride); measured on MI355X, 8 ranks x 735M fp32: 7.50-7.57 ms at
  * the pick against 7.86 ms for separate allocations and 8.35 ms for
  * rar_rank_stride.  RAR_EINVAL: NULL stride_bytes or pool, N outside
@@ -171,9 +178,10 @@ rar_status rar_rank_stride_tune(int N, int64_t P, rar_dtype dtype, void *pool, i
 
 /* rar_rank_stride_tune, also reporting what it measured: *n_candidates
  * receives K, the number of candidates timed (0 when N == 1 or P == 0), and
- * for k < K cand_stride[k], median_ms[k] and spread_ms[k] (the range of the
- * middle six of candidate k's eight timings).  The arrays hold
- * max_candidates entries; any of these outputs may be NULL. */
+ * for k < K cand_stride[k], median_ms[k] and spread_ms[k], over all of
+ * candidate k's timings (8, or 24 for a finalist; the spread is the range of
+ * their middle three quarters).  The arrays hold max_candidates entries; any
+ * of these outputs may be NULL. */
 rar_status rar_rank_stride_tune_stats(int N, int64_t P, rar_dtype dtype, void *pool, int64_t pool_bytes,
                                       int max_candidates, void *stream, int64_t *stride_bytes,
                                       int *n_candidates, int64_t cand_stride[], float median_ms[],

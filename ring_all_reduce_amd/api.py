@@ -150,7 +150,7 @@ def rar_rank_stride(P: int, dtype: int = F32) -> int:
     return out.value
 
 
-def rar_rank_stride_tune(N: int, P: int, dtype: int, pool, candidates: int = 12, stream=None) -> int:
+def rar_rank_stride_tune(N: int, P: int, dtype: int, pool, candidates: int = 64, stream=None) -> int:
     """Measured byte distance between rank buffers carved from `pool` (a
     device tensor or pointer; its contents are overwritten).  Waits for the
     stream."""
@@ -163,7 +163,7 @@ def rar_rank_stride_tune(N: int, P: int, dtype: int, pool, candidates: int = 12,
     return out.value
 
 
-def rar_rank_stride_tune_stats(N: int, P: int, dtype: int, pool, candidates: int = 12, stream=None):
+def rar_rank_stride_tune_stats(N: int, P: int, dtype: int, pool, candidates: int = 64, stream=None):
     """rar_rank_stride_tune and its measurements: (stride, [(candidate stride,
     median ms, spread ms), ...])."""
     if not hasattr(pool, "element_size"):

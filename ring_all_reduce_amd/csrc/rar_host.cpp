@@ -332,57 +332,95 @@ extern "C" rar_status rar_rank_stride_tune_stats(int N, int64_t P, rar_dtype dty
         if (he != hipSuccess && rc == RAR_OK)
             rc = hip_failed(he);
     }
-    // four rounds, alternately forward and backward over the candidates (so a
-    // drift in the device's speed reaches all of them alike); per candidate
-    // and round one untimed call, then two timed ones.  The fast strides lie
-    // within ~1% of each other and single calls vary by about as much, so
-    // fewer samples let a middling stride win now and then.
-    constexpr int kRounds = 4, kTimed = 2;
-    float ms[kMaxStrideCandidates][kRounds * kTimed] = {};
+    // Two stages.  Stage 1 times every candidate in four rounds, alternately
+    // forward and backward over the candidates (so a drift in the device's
+    // speed reaches all of them alike); per candidate and round one untimed
+    // call, then two timed ones.  The fast strides lie within ~1% of each
+    // other and single calls vary by about as much, so stage 2 times the
+    // finalists -- the four with the smallest stage-1 medians, and the static
+    // rule's stride -- in eight more rounds the same way: 24 timings each.
+    constexpr int kRounds1 = 4, kRounds2 = 8, kTimed = 2, kFinalists = 4;
+    constexpr int kMaxSamples = (kRounds1 + kRounds2) * kTimed;
+    float ms[kMaxStrideCandidates][kMaxSamples] = {};
+    int ns[kMaxStrideCandidates] = {};
     void *bufs[kMaxRanks];
     hipStream_t st = static_cast<hipStream_t>(stream);
-    for (int r = 0; r < kRounds && rc == RAR_OK; ++r)
-        for (int i = 0; i < K && rc == RAR_OK; ++i) {
-            const int k = r % 2 == 0 ? i : K - 1 - i;
-            for (int n = 0; n < N; ++n)
-                bufs[n] = static_cast<char *>(pool) + (int64_t)n * (s0 + 2 * MiB * k);
-            rc = rar_allreduce_mean(pl, bufs, P, stream);
-            for (int t = 0; t < kTimed && rc == RAR_OK; ++t) {
-                hipError_t he = hipEventRecord(ev[0], st);
-                if (he == hipSuccess && (rc = rar_allreduce_mean(pl, bufs, P, stream)) != RAR_OK)
-                    break;
-                if (he == hipSuccess)
-                    he = hipEventRecord(ev[1], st);
-                if (he == hipSuccess)
-                    he = hipEventSynchronize(ev[1]);
-                if (he == hipSuccess)
-                    he = hipEventElapsedTime(&ms[k][r * kTimed + t], ev[0], ev[1]);
-                if (he != hipSuccess)
-                    rc = hip_failed(he);
-            }
+    auto time_candidate = [&](int k) {
+        for (int n = 0; n < N; ++n)
+            bufs[n] = static_cast<char *>(pool) + (int64_t)n * (s0 + 2 * MiB * k);
+        rc = rar_allreduce_mean(pl, bufs, P, stream);
+        for (int t = 0; t < kTimed && rc == RAR_OK; ++t) {
+            hipError_t he = hipEventRecord(ev[0], st);
+            if (he == hipSuccess && (rc = rar_allreduce_mean(pl, bufs, P, stream)) != RAR_OK)
+                break;
+            if (he == hipSuccess)
+                he = hipEventRecord(ev[1], st);
+            if (he == hipSuccess)
+                he = hipEventSynchronize(ev[1]);
+            if (he == hipSuccess)
+                he = hipEventElapsedTime(&ms[k][ns[k]++], ev[0], ev[1]);
+            if (he != hipSuccess)
+                rc = hip_failed(he);
         }
+    };
+    // per candidate: the median of its timings (the mean of the middle two)
+    // and their spread (the range of the middle three quarters)
+    float med[kMaxStrideCandidates] = {}, spread[kMaxStrideCandidates] = {};
+    auto summarise = [&](int k) {
+        float t[kMaxSamples];
+        const int n = ns[k];
+        std::copy(ms[k], ms[k] + n, t);
+        std::sort(t, t + n);
+        med[k] = 0.5f * (t[n / 2 - 1] + t[n / 2]);
+        spread[k] = t[n - 1 - n / 8] - t[n / 8];
+    };
+    for (int r = 0; r < kRounds1 && rc == RAR_OK; ++r)
+        for (int i = 0; i < K && rc == RAR_OK; ++i)
+            time_candidate(r % 2 == 0 ? i : K - 1 - i);
+    int64_t fixed = 0;
+    (void)rar_rank_stride(P, dtype, &fixed);
+    const int64_t si = (fixed - s0) / (2 * MiB);
+    const bool static_is_candidate = si >= 0 && si < K;
+    int fin[kFinalists + 1], nfin = 0;
     if (rc == RAR_OK) {
-        // per candidate: the median of the eight timings (the mean of the
-        // middle two) and their spread (the range of the middle six).  The
-        // smallest median wins (ties to the smaller stride) -- unless the
-        // static rule's stride (rar_rank_stride) is a candidate and lies
-        // within the larger of the two spreads of the winner, in which case
-        // the measurement cannot tell them apart and the static stride stays.
-        constexpr int kSamples = kRounds * kTimed;
-        float med[kMaxStrideCandidates], spread[kMaxStrideCandidates];
-        int best = 0;
+        int order[kMaxStrideCandidates];
         for (int k = 0; k < K; ++k) {
-            float *t = ms[k];
-            std::sort(t, t + kSamples);
-            med[k] = 0.5f * (t[kSamples / 2 - 1] + t[kSamples / 2]);
-            spread[k] = t[kSamples - 2] - t[1];
-            if (med[k] < med[best])
-                best = k;
+            summarise(k);
+            order[k] = k;
         }
-        int64_t fixed = 0;
-        (void)rar_rank_stride(P, dtype, &fixed);
-        const int64_t si = (fixed - s0) / (2 * MiB);
-        if (si >= 0 && si < K && si != best && med[si] - med[best] <= std::max(spread[si], spread[best]))
+        std::stable_sort(order, order + K, [&](int a, int b) { return med[a] < med[b]; });
+        for (int i = 0; i < std::min(K, kFinalists); ++i)
+            fin[nfin++] = order[i];
+        if (static_is_candidate && std::find(fin, fin + nfin, (int)si) == fin + nfin)
+            fin[nfin++] = (int)si;
+        std::sort(fin, fin + nfin);
+    }
+    for (int r = 0; r < kRounds2 && rc == RAR_OK; ++r)
+        for (int i = 0; i < nfin && rc == RAR_OK; ++i)
+            time_candidate(fin[r % 2 == 0 ? i : nfin - 1 - i]);
+    if (rc == RAR_OK) {
+        // The finalist with the smallest median over its 24 timings wins
+        // (ties to the smaller stride) -- unless the static rule's stride
+        // exceeds it by no more than a third of the finalists' typical spread
+        // (the median of their spreads).  That is about two standard errors
+        // of a difference of two medians of 24 timings (the middle three
+        // quarters span about 2.3 standard deviations of one timing, and the
+        // median of 24 has a standard error of about a quarter of one), so a
+        // smaller gap is not a measured improvement and the static stride
+        // stays.  The typical spread, not the static stride's own, is the
+        // yardstick: a layout whose calls vary more than the others' is
+        // itself the slower one, and the static stride at 10 x 300M is one.
+        float fs[kFinalists + 1];
+        int best = fin[0];
+        for (int i = 0; i < nfin; ++i) {
+            summarise(fin[i]);
+            fs[i] = spread[fin[i]];
+            if (med[fin[i]] < med[best])
+                best = fin[i];
+        }
+        std::sort(fs, fs + nfin);
+        const float typical = nfin % 2 ? fs[nfin / 2] : 0.5f * (fs[nfin / 2 - 1] + fs[nfin / 2]);
+        if (static_is_candidate && si != best && med[si] - med[best] <= typical / 3.0f)
             best = (int)si;
         *stride_bytes = s0 + 2 * MiB * best;
         if (n_candidates)
