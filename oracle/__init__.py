@@ -25,10 +25,13 @@ Short names:
   [TrainMGPU]  "[AI System] Training With Multiple GPUs".
   [DDPpage]    "[PyTorch] GPU 분산 학습 1 - DP / DDP / FSDP 개념".
 
-Parity pinned (see tests/test_oracle_pins.py) except for two conventions the
-pages leave open: how the mean rounds (binary32 S/N, not S*(1/N)) and how the
-SGD product and difference round (two roundings, no FMA).  Those two are
-"parity unpinned" beyond their special cases (N a power of two, lr = 0).
+Parity pinned (see tests/test_oracle_pins.py), including the two conventions
+the pages leave open.  The mean is one correctly rounded binary32 quotient
+S/N, not S*(1/N): pinned by integer inputs whose exact mean is known, and by a
+case where the two differ.  The SGD update rounds the product lr*m and then
+the difference w - (lr*m), with no fused multiply-add: pinned by hand-derived
+cases that tell the two apart and by an element-wise check against exact
+rational arithmetic.
 """
 from __future__ import annotations
 
