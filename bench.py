@@ -95,7 +95,7 @@ def tuned_pool(wl, dev, stream, P=None, N=None):
 
 def layout_note(stride, P, dt, full=False):
     """The rank layout and what the tuner measured: the picked and the static
-    stride's median and spread (range of the middle six of eight timings) of
+    stride's median and spread (range of the middle three quarters of its timings) of
     the fused mean, and with full=True every candidate's."""
     from ring_all_reduce_amd import api
     static = api.rar_rank_stride(P, dt)
