@@ -132,9 +132,13 @@ def committed_traffic(workload_name: str, dtype: str = "f32"):
     return d.get("hbm_bytes_per_launch")
 
 
-def time_launches(fn, steps, warmup, stream):
+def time_launches(fn, steps, warmup, stream, prime=False):
     """Run fn() warmup times, then time `steps` calls: per-call HIP events on
-    `stream` (the library's launch stream) plus one event pair around all."""
+    `stream` (the library's launch stream) plus one event pair around all.
+    prime=True enqueues one more untimed call after the synchronisation, so
+    that the host's preparation of the first timed call overlaps device work
+    instead of showing as idle time inside the timed region (as it would in
+    a training loop, where the previous call is still running)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -142,6 +146,8 @@ def time_launches(fn, steps, warmup, stream):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if prime:
+        fn()
     t0 = time.perf_counter()
     a.record(stream)
     for i in range(steps):
@@ -454,7 +460,7 @@ def secondary_rows(dev, stream, reps=5):
     rows = []
 
     def add(name, nbytes, fn, moved=None, extra=None, oracle_leg=None):
-        total, per, _ = time_launches(fn, reps, 2, stream)
+        total, per, _ = time_launches(fn, reps, 2, stream, prime=True)
         ms = total / reps
         r = {"row": name, "ms": round(ms, 4), "ms_median": round(statistics.median(per), 4),
              "ms_min": round(min(per), 4), "alg_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
