@@ -1192,21 +1192,25 @@ bool tensors_form_arenas(rar_buckets_t b, int N, void *const tensors[], char *ba
     if ((b->per_bucket * es) % 16 != 0)
         return false;
     for (int n = 0; n < N; ++n) {
-        char *b0 = nullptr;
+        // addresses as integers: the call is validated only afterwards, so a
+        // pointer here may be null
+        uintptr_t b0 = 0;
         int64_t cum = 0;
         for (int t = 0; t < b->n_tensors; ++t) {
             if (b->numel[t] > 0) {
-                char *p = static_cast<char *>(tensors[(int64_t)n * b->n_tensors + t]);
+                const uintptr_t p = reinterpret_cast<uintptr_t>(tensors[(int64_t)n * b->n_tensors + t]);
+                if (!p)
+                    return false;
                 if (!b0)
                     b0 = p;  // every earlier tensor is empty: this one starts the arena
-                if (p != b0 + cum * es)
+                if (p != b0 + (uintptr_t)cum * es)
                     return false;
             }
             cum += b->numel[t];
         }
-        if (!b0 || ((uintptr_t)b0 & 15))
+        if (!b0 || (b0 & 15))
             return false;
-        base[n] = b0;
+        base[n] = reinterpret_cast<char *>(b0);
     }
     return true;
 }
