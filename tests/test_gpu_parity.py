@@ -3,10 +3,12 @@
 Binary32 results must be bit-identical to the oracle (same ring order, same
 IEEE operations).  bf16 results must be bit-identical to the oracle's bf16
 variant and within 1e-2 of a float64 mean (max |error| / max |mean|).  Small
-and ragged cases run the oracle in full; the full-size workloads compare
-sampled elements (every chunk boundary +-9 and 10^6 random ones) through the
-oracle's literal ring restricted to those elements, plus whole-array
-properties (all ranks identical).
+and ragged cases run the oracle in full.  The full-size workloads are checked
+twice: on sampled elements (every chunk boundary +-9 and 10^6 random ones)
+through the oracle's literal ring restricted to those elements, plus
+whole-array properties (all ranks identical); and on every element of every
+rank, in the benchmark's layout and launch shape, against the oracle run over
+the whole workload.
 """
 import pathlib
 
