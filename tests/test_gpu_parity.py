@@ -1512,9 +1512,11 @@ def test_full_size_every_element(key):
 
 def test_full_size_transformer_buckets_every_element():
     """The 8-rank Transformer at full size (118 buckets of 25 MB, arenas at the
-    benchmark's tuned stride), reduced straight from the tensor lists, as
-    arena slices, and packed through the ring steps: every element of every
-    tensor bit-exact against the oracle's bucket-by-bucket literal ring."""
+    benchmark's tuned stride), reduced by the fused pass straight from the
+    tensor lists and as arena slices, and through the ring steps from the
+    tensor lists (which lie end to end, so they take the arena launches and
+    leave the bucket buffers unused): every element of every tensor
+    bit-exact against the oracle's bucket-by-bucket literal ring."""
     wl = synth.WORKLOADS[4]
     stride, pool = _tuned_layout(wl, wl.P, wl.N)
     specs, ranks = synth.transformer_rank_tensors(wl, DEV, pool=pool, stride_bytes=stride)
