@@ -341,6 +341,26 @@ def test_bucket_calls_validate_arguments_even_without_buckets():
     assert L.rar_bucket_allreduce_mean(b.handle, 2, 0, 0, empty, None, None) == api.OK
 
 
+def test_null_tensor_pointers_are_rejected_before_any_device_work():
+    """Tensor lists with null pointers, for every algorithm: the check of
+    whether the lists lie end to end (made before validation) treats them as
+    no arena, and validation rejects the call.  Run on the CPU, so nothing may
+    reach a launch."""
+    L = lib()
+    for dt in (api.F32, api.BF16):
+        b = api.rar_bucket_plan([100, 0, 60, 4], dt, 64)
+        N = 3
+        null = api._ptr_array([None] * (N * 4))
+        # first rank's tensors end to end, the others null
+        es = 4 if dt == api.F32 else 2
+        part = api._ptr_array([FAKE, FAKE + 100 * es, FAKE + 100 * es, FAKE + 160 * es] + [None] * (2 * 4))
+        for algo in (api.FUSED, api.RING, api.NAIVE):
+            if dt == api.BF16 and algo == api.NAIVE:
+                continue
+            for tensors in (null, part):
+                assert L.rar_bucket_allreduce_mean(b.handle, N, api.BALANCED, algo, tensors, None, None) == api.EINVAL
+
+
 def test_binding_rejects_ragged_tensor_lists_and_short_event_lists():
     b = api.rar_bucket_plan([10, 20], api.F32, 4 * 16)
     ragged = [[FAKE, FAKE + 4096], [FAKE + 8192]]
