@@ -83,9 +83,7 @@ def tuned_pool(wl, dev, stream, P=None, N=None):
     P = wl.P if P is None else P
     N = wl.N if N is None else N
     dt, es = (api.F32, 4) if wl.dtype == "f32" else (api.BF16, 2)
-    MiB = 1 << 20
-    s0 = max(2 * MiB, -(-P * es // (2 * MiB)) * 2 * MiB)
-    smax = s0 + 2 * MiB * (TUNE_CANDIDATES - 1)
+    smax = api.rar_rank_stride_candidate(P, dt, TUNE_CANDIDATES - 1)
     pool = torch.zeros(synth.pool_elements(wl, smax, P, N), dtype=torch.float32 if es == 4 else torch.bfloat16,
                        device=dev)
     stride, cands = api.rar_rank_stride_tune_stats(N, P, dt, pool, TUNE_CANDIDATES, stream)

@@ -143,13 +143,25 @@ rar_status rar_plan(int N, int64_t P, rar_dtype dtype, rar_chunking chunking, ra
  * overflows. */
 rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *stride_bytes);
 
+/* The stride candidates rar_rank_stride_tune times, so that a caller can size
+ * its pool: *stride_bytes receives candidate k (0 <= k <
+ * RAR_MAX_STRIDE_CANDIDATES) for ranks of P elements of dtype.  With s0 the
+ * smallest multiple of 2 MiB >= P * element size, candidates 0..31 are s0,
+ * s0 + 2 MiB, ..., s0 + 62 MiB, and candidates 32..63 are the multiples of
+ * 8 MiB from the first one >= s0 + 64 MiB, 8 MiB apart.  They increase with
+ * k; rar_rank_stride's stride is candidate 0 or 1.  A pool for the first K
+ * candidates needs (N-1) * candidate(K-1) + P * element size bytes.  Host
+ * only, no HIP call.  RAR_EINVAL: NULL stride_bytes, unknown dtype, P < 0, k
+ * out of range, or P too large. */
+rar_status rar_rank_stride_candidate(int64_t P, rar_dtype dtype, int k, int64_t *stride_bytes);
+
 /* Not an operation of the pages either: measured layout advice for the same
  * single-allocation placement.  Times the fused mean over N ranks carved
- * from `pool` (device, 16-byte aligned, pool_bytes long) at the strides s0,
- * s0 + 2 MiB, ... (s0 the smallest multiple of 2 MiB >= P * element size),
- * the first max_candidates (1..RAR_MAX_STRIDE_CANDIDATES) of them for which
- * (N-1) * stride + P * element size <= pool_bytes, and returns the fastest
- * in *stride_bytes.  Two stages, each in rounds that visit the candidates
+ * from `pool` (device, 16-byte aligned, pool_bytes long) at the strides
+ * rar_rank_stride_candidate gives, the first max_candidates
+ * (1..RAR_MAX_STRIDE_CANDIDATES) of them for which (N-1) * stride + P *
+ * element size <= pool_bytes, and returns the fastest in *stride_bytes.
+ * Two stages, each in rounds that visit the candidates
  * forward and backward in turn, one untimed and two timed calls per
  * candidate and round: four rounds over every candidate, then eight more
  * over the finalists, the four with the smallest medians so far and the
@@ -160,10 +172,11 @@ rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *stride_bytes);
  * median of their spreads, each the range of the middle three quarters of
  * its timings), about two standard errors of a difference of two such
  * medians: on MI355X the fast strides lie within about 1% of each other,
- * about as much as single calls vary.  Fast strides can lie well past the
- * first few: at
- * 10 x 300M fp32 the fastest of 64 were 1192 and 1272 MiB (the 64th), the
- * SGD call up to 2% faster there than at the static rule's 1146 MiB.  The
+ * about as much as single calls vary.  Fast strides also lie beyond the
+ * first few: at 10 x 300M fp32 the best of a sweep from 1146 to 1658 MiB
+ * were 1280 and 1368 MiB, the SGD call 1% faster there than at the best
+ * stride within 1146-1272 MiB and 2.5% faster than at the static rule's
+ * 1146 MiB (one box, interleaved rounds).  The
  * pool's contents are overwritten; the call enqueues on `stream` and waits
  * for it, so it must not run under graph capture.  N == 1 or P == 0 returns
  * s0 without device work.  Which strides are fast differs by shape (see
@@ -361,7 +374,8 @@ const char *rar_strerror(rar_status s);
 
 /* Library version as major*10000 + minor*100 + patch (0.2.0 = 200 adds
  * rar_rank_stride, 0.3.0 = 300 rar_rank_stride_tune, 0.4.0 = 400
- * rar_allreduce_ring_noalloc, 0.5.0 = 500 rar_rank_stride_tune_stats). */
+ * rar_allreduce_ring_noalloc, 0.5.0 = 500 rar_rank_stride_tune_stats,
+ * 0.6.0 = 600 rar_rank_stride_candidate and the wider stride search). */
 int rar_version(void);
 
 #ifdef __cplusplus

@@ -21,6 +21,7 @@ SIGNATURES = {
     "rar_plan": (_int, [_int, _i64, _int, _int, ctypes.POINTER(_vp)]),
     "rar_plan_destroy": (_int, [_vp]),
     "rar_rank_stride": (_int, [_i64, _int, _i64p]),
+    "rar_rank_stride_candidate": (_int, [_i64, _int, _int, _i64p]),
     "rar_rank_stride_tune": (_int, [_int, _i64, _int, _vp, _i64, _int, _vp, _i64p]),
     "rar_rank_stride_tune_stats": (_int, [_int, _i64, _int, _vp, _i64, _int, _vp, _i64p, _ip, _i64p,
                                           ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),

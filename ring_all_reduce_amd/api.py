@@ -24,6 +24,7 @@ BALANCED, CEIL, ALIGN16 = 0, 1, 2
 FUSED, RING, NAIVE = 0, 1, 2
 OK, EINVAL, EMISMATCH, EALIGN, ENOMEM, EHIP, ETOOLARGE = 0, -1, -2, -3, -4, -5, -6
 MAX_RANKS = 64
+MAX_STRIDE_CANDIDATES = 64
 STATIC_WS_ELEMS = 1 << 24
 
 
@@ -147,6 +148,14 @@ def rar_rank_stride(P: int, dtype: int = F32) -> int:
     """Recommended byte distance between rank buffers carved from one allocation."""
     out = ctypes.c_int64()
     _check(lib().rar_rank_stride(int(P), int(dtype), ctypes.byref(out)), "rar_rank_stride")
+    return out.value
+
+
+def rar_rank_stride_candidate(P: int, dtype: int, k: int) -> int:
+    """Candidate k of the strides rar_rank_stride_tune times (for sizing its pool)."""
+    out = ctypes.c_int64()
+    _check(lib().rar_rank_stride_candidate(int(P), int(dtype), int(k), ctypes.byref(out)),
+           "rar_rank_stride_candidate")
     return out.value
 
 

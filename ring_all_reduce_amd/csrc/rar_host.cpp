@@ -62,6 +62,24 @@ void cut_chunks(int N, int64_t P, rar_chunking mode, int es, rar::ChunkTable &ct
 
 int block_budget(const rar_plan_s *pl) { return pl->max_blocks > 0 ? pl->max_blocks : kDefaultBlocks; }
 
+// Stride candidates of the layout tuner for ranks of `need` bytes: the first
+// kFineCandidates at 2 MiB steps from s0 (the smallest multiple of 2 MiB >=
+// need), then multiples of 8 MiB from the first one >= s0 + 2 MiB *
+// kFineCandidates, at 8 MiB steps.  Measured on MI355X the fast strides lie
+// both near s0 and further out, and those further out are multiples of 8 MiB.
+constexpr int kFineCandidates = 32;
+constexpr int64_t kMiB = int64_t(1) << 20;
+
+int64_t stride_base(int64_t need) { return std::max<int64_t>(2 * kMiB, (need + 2 * kMiB - 1) / (2 * kMiB) * (2 * kMiB)); }
+
+int64_t stride_candidate(int64_t s0, int k)
+{
+    if (k < kFineCandidates)
+        return s0 + 2 * kMiB * k;
+    const int64_t c0 = (s0 + 2 * kMiB * kFineCandidates + 8 * kMiB - 1) / (8 * kMiB) * (8 * kMiB);
+    return c0 + 8 * kMiB * (k - kFineCandidates);
+}
+
 rar_status hip_status(hipError_t e) { return e == hipSuccess ? RAR_OK : RAR_EHIP; }
 
 // A failed HIP runtime call also sets HIP's per-thread "last error", which
@@ -287,6 +305,15 @@ extern "C" rar_status rar_rank_stride(int64_t P, rar_dtype dtype, int64_t *strid
     return RAR_OK;
 }
 
+extern "C" rar_status rar_rank_stride_candidate(int64_t P, rar_dtype dtype, int k, int64_t *stride_bytes)
+{
+    if (!stride_bytes || !valid_dtype(dtype) || P < 0 || k < 0 || k >= kMaxStrideCandidates ||
+        P > (INT64_MAX / 4) / elem_bytes(dtype))
+        return RAR_EINVAL;
+    *stride_bytes = stride_candidate(stride_base(P * elem_bytes(dtype)), k);
+    return RAR_OK;
+}
+
 extern "C" rar_status rar_rank_stride_tune(int N, int64_t P, rar_dtype dtype, void *pool, int64_t pool_bytes,
                                            int max_candidates, void *stream, int64_t *stride_bytes)
 {
@@ -299,13 +326,11 @@ extern "C" rar_status rar_rank_stride_tune_stats(int N, int64_t P, rar_dtype dty
                                                  int *n_candidates, int64_t cand_stride[], float median_ms[],
                                                  float spread_ms[])
 {
-    constexpr int64_t MiB = int64_t(1) << 20;
     if (!stride_bytes || N < 1 || N > kMaxRanks || P < 0 || !valid_dtype(dtype) || max_candidates < 1 ||
         max_candidates > kMaxStrideCandidates || pool_bytes < 0 || P > (INT64_MAX / 4) / elem_bytes(dtype))
         return RAR_EINVAL;
     const int64_t need = P * elem_bytes(dtype);
-    // candidates: the multiples of 2 MiB from the smallest one >= need
-    const int64_t s0 = std::max<int64_t>(2 * MiB, (need + 2 * MiB - 1) / (2 * MiB) * (2 * MiB));
+    const int64_t s0 = stride_base(need);
     if (n_candidates)
         *n_candidates = 0;
     if (N == 1 || P == 0) {  // nothing to place relative to anything
@@ -317,7 +342,7 @@ extern "C" rar_status rar_rank_stride_tune_stats(int N, int64_t P, rar_dtype dty
     if ((uintptr_t)pool & 15)
         return RAR_EALIGN;
     int K = 0;  // candidates whose N ranks fit in the pool
-    while (K < max_candidates && need <= pool_bytes && s0 + 2 * MiB * K <= (pool_bytes - need) / (N - 1))
+    while (K < max_candidates && need <= pool_bytes && stride_candidate(s0, K) <= (pool_bytes - need) / (N - 1))
         ++K;
     if (K == 0)
         return RAR_EINVAL;
@@ -347,7 +372,7 @@ extern "C" rar_status rar_rank_stride_tune_stats(int N, int64_t P, rar_dtype dty
     hipStream_t st = static_cast<hipStream_t>(stream);
     auto time_candidate = [&](int k) {
         for (int n = 0; n < N; ++n)
-            bufs[n] = static_cast<char *>(pool) + (int64_t)n * (s0 + 2 * MiB * k);
+            bufs[n] = static_cast<char *>(pool) + (int64_t)n * stride_candidate(s0, k);
         rc = rar_allreduce_mean(pl, bufs, P, stream);
         for (int t = 0; t < kTimed && rc == RAR_OK; ++t) {
             hipError_t he = hipEventRecord(ev[0], st);
@@ -379,8 +404,11 @@ extern "C" rar_status rar_rank_stride_tune_stats(int N, int64_t P, rar_dtype dty
             time_candidate(r % 2 == 0 ? i : K - 1 - i);
     int64_t fixed = 0;
     (void)rar_rank_stride(P, dtype, &fixed);
-    const int64_t si = (fixed - s0) / (2 * MiB);
-    const bool static_is_candidate = si >= 0 && si < K;
+    int si = -1;
+    for (int k = 0; k < K; ++k)
+        if (stride_candidate(s0, k) == fixed)
+            si = k;
+    const bool static_is_candidate = si >= 0;
     int fin[kFinalists + 1], nfin = 0;
     if (rc == RAR_OK) {
         int order[kMaxStrideCandidates];
@@ -391,8 +419,8 @@ extern "C" rar_status rar_rank_stride_tune_stats(int N, int64_t P, rar_dtype dty
         std::stable_sort(order, order + K, [&](int a, int b) { return med[a] < med[b]; });
         for (int i = 0; i < std::min(K, kFinalists); ++i)
             fin[nfin++] = order[i];
-        if (static_is_candidate && std::find(fin, fin + nfin, (int)si) == fin + nfin)
-            fin[nfin++] = (int)si;
+        if (static_is_candidate && std::find(fin, fin + nfin, si) == fin + nfin)
+            fin[nfin++] = si;
         std::sort(fin, fin + nfin);
     }
     for (int r = 0; r < kRounds2 && rc == RAR_OK; ++r)
@@ -421,13 +449,13 @@ extern "C" rar_status rar_rank_stride_tune_stats(int N, int64_t P, rar_dtype dty
         std::sort(fs, fs + nfin);
         const float typical = nfin % 2 ? fs[nfin / 2] : 0.5f * (fs[nfin / 2 - 1] + fs[nfin / 2]);
         if (static_is_candidate && si != best && med[si] - med[best] <= typical / 3.0f)
-            best = (int)si;
-        *stride_bytes = s0 + 2 * MiB * best;
+            best = si;
+        *stride_bytes = stride_candidate(s0, best);
         if (n_candidates)
             *n_candidates = K;
         for (int k = 0; k < K; ++k) {
             if (cand_stride)
-                cand_stride[k] = s0 + 2 * MiB * k;
+                cand_stride[k] = stride_candidate(s0, k);
             if (median_ms)
                 median_ms[k] = med[k];
             if (spread_ms)
@@ -1356,4 +1384,4 @@ extern "C" const char *rar_strerror(rar_status s)
     return "unknown status";
 }
 
-extern "C" int rar_version(void) { return 500; }  // 0.5.0: rar_rank_stride_tune_stats added
+extern "C" int rar_version(void) { return 600; }  // 0.6.0: rar_rank_stride_candidate, wider stride search

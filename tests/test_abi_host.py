@@ -442,6 +442,28 @@ def test_rank_stride_is_two_mib_modulo_four_and_covers_the_buffer():
     assert L.rar_rank_stride((1 << 62), 0, ctypes.byref(out)) == api.EINVAL
 
 
+def test_rank_stride_candidates():
+    """The tuner's candidate strides: 32 at 2 MiB steps from the smallest
+    multiple of 2 MiB that holds a rank, then 32 multiples of 8 MiB from the
+    first one at least 64 MiB past it; rar_rank_stride's stride among the
+    first two."""
+    MiB = 1 << 20
+    for P, dt in ((300_000_000, api.F32), (100_000_000, api.BF16), (11_700_000, api.F32), (1, api.F32), (0, api.BF16),
+                  (735_371_264, api.F32)):
+        es = 4 if dt == api.F32 else 2
+        s0 = max(2 * MiB, -(-P * es // (2 * MiB)) * 2 * MiB)
+        c = [api.rar_rank_stride_candidate(P, dt, k) for k in range(api.MAX_STRIDE_CANDIDATES)]
+        assert c[:32] == [s0 + 2 * MiB * k for k in range(32)]
+        c0 = -(-(s0 + 64 * MiB) // (8 * MiB)) * 8 * MiB
+        assert c[32:] == [c0 + 8 * MiB * k for k in range(32)]
+        assert all(a < b for a, b in zip(c, c[1:])) and c[0] >= P * es
+        assert api.rar_rank_stride(P, dt) in c[:2]
+    for args in ((-1, api.F32, 0), (10, 7, 0), (10, api.F32, -1), (10, api.F32, api.MAX_STRIDE_CANDIDATES)):
+        with pytest.raises(api.RarError):
+            api.rar_rank_stride_candidate(*args)
+    assert lib().rar_rank_stride_candidate(10, api.F32, 0, None) == api.EINVAL
+
+
 def test_rank_stride_tune_validates_before_any_device_work():
     """Only calls that must return before device work (FAKE is never
     dereferenced); the measurement itself runs on the GPU."""

@@ -1381,6 +1381,7 @@ def test_rank_stride_tune_picks_a_fitting_candidate_and_stays_exact(key):
     N, P, K = 6, 1_000_003, 4
     s0 = -(-P * es // (2 * MiB)) * 2 * MiB
     cands = [s0 + 2 * MiB * k for k in range(K)]
+    assert cands == [api.rar_rank_stride_candidate(P, dt, k) for k in range(K)]
     pool = torch.zeros(synth.pool_elements(wl, cands[-1] + 2 * MiB, P, N), dtype=tdt, device=DEV)
     stride = api.rar_rank_stride_tune(N, P, dt, pool, candidates=K + 1)
     assert stride in cands + [cands[-1] + 2 * MiB]
@@ -1408,6 +1409,13 @@ def test_rank_stride_tune_picks_a_fitting_candidate_and_stays_exact(key):
     with pytest.raises(api.RarError) as e:
         api.rar_rank_stride_tune(N, P, dt, exact[:-1], candidates=K)
     assert e.value.status == api.EINVAL
+    # a pool holding 36 candidates: the tuner times exactly the library's candidate strides
+    wide = torch.zeros(synth.pool_elements(wl, api.rar_rank_stride_candidate(P, dt, 35), P, N), dtype=tdt,
+                       device=DEV)
+    pick, stats = api.rar_rank_stride_tune_stats(N, P, dt, wide, candidates=64)
+    assert [c for c, _, _ in stats] == [api.rar_rank_stride_candidate(P, dt, k) for k in range(36)]
+    assert pick in [c for c, _, _ in stats]
+    del wide
     torch.cuda.synchronize()
     bufs = synth.rank_gradients_in_pool(wl, stride, DEV, P=P, N=N, pool=pool)
     w = synth.weights(wl, DEV, P=P)
@@ -1469,12 +1477,10 @@ def test_bucket_jobs_merge_only_across_contiguous_tensors(layout):
 def _tuned_layout(wl, P, N, candidates=64):
     """The rank placement bench.py times: one pool, the stride the library
     measures fastest among `candidates` (the benchmark's 64)."""
-    MiB = 1 << 20
-    es = 4 if wl.dtype == "f32" else 2
-    s0 = -(-P * es // (2 * MiB)) * 2 * MiB
-    pool = torch.zeros(synth.pool_elements(wl, s0 + 2 * MiB * (candidates - 1), P, N),
-                       dtype=torch.float32 if es == 4 else torch.bfloat16, device=DEV)
-    stride = api.rar_rank_stride_tune(N, P, api.F32 if es == 4 else api.BF16, pool, candidates)
+    dt = api.F32 if wl.dtype == "f32" else api.BF16
+    pool = torch.zeros(synth.pool_elements(wl, api.rar_rank_stride_candidate(P, dt, candidates - 1), P, N),
+                       dtype=torch.float32 if dt == api.F32 else torch.bfloat16, device=DEV)
+    stride = api.rar_rank_stride_tune(N, P, dt, pool, candidates)
     return stride, pool
 
 
